@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for paged KV-cache attention on one MI355X.
+
+One step = the cache write of each sequence's new token (pa_reshape_and_cache)
+followed by paged decode attention over every sequence's context
+(pa_decode_partitioned by default, pa_decode with --kernel single). The
+default workload is the Llama-8B-shaped GQA batch: 64 sequences, 32 query /
+8 KV heads, head size 128, bf16 KV, context lengths min(4096, 100 +
+floor(Exp(mean 400))), 16-token blocks scattered through a pool twice the size
+needed. Inputs are synthetic (seeded N(0, 1) values) and already resident in
+HBM when timing starts.
+
+The KV working set of one step (~131 MB) fits in the 256 MB Infinity Cache, so
+consecutive steps rotate over R independent replicas of the batch (same
+lengths, different block placement and values; R * 131 MB >> 256 MB).
+
+Printed: one JSON line on stdout. `value` is KV-read GB/s of whole steps
+(scatter + attention, launch gaps included); `roofline` is the attention call
+alone, timed with HIP events on the launch stream; `cpu_baseline` is the fp64
+oracle on the host cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attention KV-read GB/s (% of HBM peak) and seq-steps/sec at 1 GPU"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_456_amd", "csrc", "pa_decode.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str, partition_size: int):
+    """HBM bytes per attention call from a committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except ValueError:
+        return None
+    key = f"{workload}/{kernel}/{partition_size}"
+    ent = rec.get("entries", {}).get(key)
+    if not ent or ent.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_call")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="llama8b_gqa_bf16")
+    ap.add_argument("--kernel", choices=("partitioned", "single"), default="partitioned")
+    ap.add_argument("--partition-size", type=int, default=0, help="0 = the workload's default")
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of the CPU oracle baseline (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_456_amd as pa
+    from paged_kv_cache_456_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pa.load()
+    dev = torch.device("cuda:0")
+    spec = wl.SPECS[args.workload]
+    psize = args.partition_size or spec.partition_size
+
+    # Replicas of the batch: same lengths, independent placement and values.
+    base = wl.make_workload(args.workload, device=dev)
+    lengths = base.context_lens.tolist()
+    reps = [base] + [wl.make_workload(args.workload, device=dev, lengths=lengths, seed_offset=r)
+                     for r in range(1, args.replicas)]
+    S, Hq, D = base.query.shape
+    Hkv = spec.num_kv_heads
+    kv_bytes = base.kv_bytes()
+    mcl = base.max_context_len
+    ws_bytes = pa.pa_decode_partitioned_workspace_size(S, Hq, D, mcl, psize)
+    inputs = []
+    for w in reps:
+        inputs.append(dict(
+            w=w, bt=torch.from_numpy(w.block_tables).to(dev), cl=torch.from_numpy(w.context_lens).to(dev),
+            slots=torch.from_numpy(w.slot_mapping).to(dev),
+            out=torch.empty((S, Hq, D), dtype=torch.float32, device=dev),
+            ws=torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    log(f"[bench] {args.workload}: S={S} Hq={Hq} Hkv={Hkv} D={D} sum(L)={int(base.context_lens.sum())} "
+        f"KV bytes/step={kv_bytes / 1e6:.1f} MB, replicas={args.replicas}, kernel={args.kernel}, P={psize}")
+
+    def attention(x):
+        w = x["w"]
+        if args.kernel == "single":
+            pa.pa_decode(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"], w.scale)
+        else:
+            pa.pa_decode_partitioned(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"],
+                                     w.scale, mcl, psize, x["ws"])
+
+    def step(i, ev=None):
+        x = inputs[i % len(inputs)]
+        w = x["w"]
+        pa.pa_reshape_and_cache(w.key, w.value, w.key_cache, w.value_cache, x["slots"])
+        if ev is not None:
+            ev[0].record()
+        attention(x)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    # Timed region: exactly K steps between two synchronisations.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    log(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    attn_ms = float(np.mean(call_ms))
+    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload, args.kernel, psize)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_size": D, "block_size": 16, "sum_context_len": int(base.context_lens.sum()),
+            "max_context_len": mcl, "kv_bytes_per_step": kv_bytes,
+            "kernel": "pa_decode" if args.kernel == "single" else "pa_decode_partitioned",
+            "partition_size": psize if args.kernel == "partitioned" else None,
+            "replicas": args.replicas, "step": "pa_reshape_and_cache + attention",
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "attention_ms_per_call": round(attn_ms, 5),
+        "attention_ms_p50": round(float(np.median(call_ms)), 5),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode attention call (partition kernel + log-sum-exp reduce)"
+                      if args.kernel == "partitioned" else "pa_decode kernel",
+        },
+        "cpu_baseline": None,
+    }
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(base, kv_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(w, kv_bytes: int, seconds: float):
+    """The fp64 oracle (cache write + decode of the whole batch) on the host cores,
+    repeated for about `seconds` of wall clock. Host copies are made first."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    B = w.block_size
+    L = w.context_lens.astype(np.int64)
+    nblk = -(-L // B)
+    blocks = np.unique(np.concatenate([w.block_tables[s, :nblk[s]] for s in range(w.num_seqs)]))
+    remap = np.full(w.num_blocks, -1, np.int64)
+    remap[blocks] = np.arange(len(blocks))
+    tables = np.full_like(w.block_tables, -1)
+    for s in range(w.num_seqs):
+        tables[s, :nblk[s]] = remap[w.block_tables[s, :nblk[s]]]
+    slots = np.where(w.slot_mapping >= 0, remap[np.maximum(w.slot_mapping, 0) // B] * B + w.slot_mapping % B, -1)
+    t_copy = time.perf_counter()
+    ids = torch.from_numpy(blocks).to(w.key_cache.device)
+    kc = w.key_cache.index_select(0, ids).cpu()
+    vc = w.value_cache.index_select(0, ids).cpu()
+    key, value, q = w.key.cpu(), w.value.cpu(), w.query.cpu()
+    t_copy = time.perf_counter() - t_copy
+    bits = (lambda t: t.view(torch.int16)) if kc.element_size() == 2 else (lambda t: t.view(torch.int32))
+    kb, vb = bits(kc).numpy(), bits(vc).numpy()
+    kn, vn = bits(key).numpy(), bits(value).numpy()
+    threads = oracle.max_threads()
+    log(f"[bench] cpu oracle: {len(blocks)} blocks copied to host in {t_copy:.2f} s, {threads} threads")
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.reshape_and_cache(kn, vn, kb, vb, slots, block_size=B)
+        oracle.decode(q, kc, vc, tables, w.context_lens, w.scale)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    log(f"[bench] cpu oracle: {n} steps in {el:.2f} s")
+    return {
+        "value": round(kv_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "seq_steps_per_s": round(w.num_seqs * n / el, 2),
+        "sample": f"{n} full decode steps of the same batch ({w.num_seqs} sequences, cache write + "
+                  f"attention, fp64, inputs in host memory), {el:.1f} s wall; device-to-host copy "
+                  f"{t_copy:.2f} s not included",
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,182 @@
+/*
+ * pa.h -- paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * A KV cache cut into fixed-size blocks of 16 tokens, scattered through one
+ * shared physical pool and reached through a per-sequence block table
+ * ("Idea 1: PagedAttention" on the day-9 post of skandtandon.pages.dev; "The
+ * idea vLLM started from: pages" on "What vLLM Is and Why It Exists"; "Paged
+ * Attention" on "vLLM Solved the Wrong Bottleneck"). This library provides
+ * the two GPU operations of one decode step over such a cache:
+ *
+ *   pa_reshape_and_cache   write each new token's key and value into its slot
+ *   pa_decode              one query token per sequence attends over its
+ *                          block-scattered context (single pass)
+ *   pa_decode_partitioned  the same result, with each context cut into
+ *                          fixed-size partitions that run in parallel and a
+ *                          log-sum-exp reduce across partitions
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  S    num_seqs            Hq  num_q_heads         Hkv num_kv_heads
+ *  D    head_size (64 or 128)                       B   block_size (must be 16)
+ *  NB   num_blocks in each pool                     MB  max_blocks_per_seq
+ *
+ *  key_cache, value_cache  [NB][Hkv][B][D], row-major, dtype kv_dtype. One
+ *                          physical block id addresses every KV head; the
+ *                          (block, head) tile is B*D contiguous elements.
+ *  block_tables            int32 [S][MB]: entry [s][j] is the physical block
+ *                          holding tokens 16j .. 16j+15 of sequence s. Only
+ *                          entries j < ceil(context_lens[s] / 16) are read.
+ *  context_lens            int32 [S]: tokens of context of each sequence,
+ *                          including the token written in this step.
+ *  query, out              [S][Hq][D]. Query head h reads KV head
+ *                          h / (Hq / Hkv) (grouped-query attention).
+ *  scale                   multiplies q.k before the softmax (typically
+ *                          1/sqrt(D)).
+ *
+ *  The attention computed, per sequence s and query head h, over the tokens
+ *  t < L = context_lens[s] (the pages give no formula; this is standard
+ *  scaled dot-product softmax attention of the new token over its context):
+ *      l_t = scale * q[s][h] . K_t,   w_t = softmax_t(l_t),   out = sum_t w_t V_t
+ *  Arithmetic is fp32 (bf16 inputs are exact in fp32). L = 0 gives a zero row.
+ *
+ *  Pointers.   All data pointers are DEVICE pointers, 16-byte aligned, owned
+ *              by the caller and kept alive until the work on `stream` has
+ *              finished. The library allocates nothing, keeps no pointer after
+ *              a call returns and holds no state; calls are thread-safe.
+ *              `out` and `workspace` must not overlap any input.
+ *  Streams.    `stream` is a hipStream_t (NULL = the default stream). Every
+ *              call only enqueues work and returns; nothing synchronises.
+ *  Errors.     Host-side checks run before anything is enqueued and return:
+ *                PA_EINVAL        null or misaligned pointer, negative count,
+ *                                 Hq not a multiple of Hkv, bad partition size
+ *                PA_EUNSUPPORTED  B != 16, D not 64 or 128, Hq/Hkv > 16,
+ *                                 an unsupported dtype
+ *                PA_EWORKSPACE    workspace smaller than required
+ *                PA_EHIP          the kernel launch failed
+ *              Device-resident inputs are not copied to the host. The kernels
+ *              check them anyway and never touch memory outside the pools:
+ *              a sequence whose context is longer than its table (or than
+ *              max_context_len), or whose table reaches a block id outside
+ *              [0, NB), gets an all-NaN output row; a slot outside the pool is
+ *              skipped by the cache write.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype_t;
+
+typedef enum {
+    PA_OK = 0,
+    PA_EINVAL = 1,
+    PA_EUNSUPPORTED = 2,
+    PA_EWORKSPACE = 3,
+    PA_EHIP = 4
+} pa_status_t;
+
+/*
+ * pa_reshape_and_cache -- write new tokens' K and V into their slots.
+ *
+ * The pages say each request keeps the key/value state of every token it has
+ * produced ("The problem a naive server has", point 3, on "What vLLM Is and
+ * Why It Exists") and holds only the blocks those tokens fill ("The idea vLLM
+ * started from: pages"). Slot numbering is a reading: slot = block * 16 +
+ * row, so token i lands in key_cache[slot / 16][h][slot % 16][:] for every
+ * KV head h.
+ *
+ *   key, value          [T][Hkv][D] of kv_dtype, T = num_tokens
+ *   key_cache, value_cache  the pools, updated in place
+ *   slot_mapping        int64 [T]; a negative slot marks a padding token and
+ *                       is skipped. Two tokens must not name the same slot.
+ *   num_blocks          NB; slots >= NB * 16 are skipped.
+ *
+ * The copy is bit-exact (no conversion: input dtype = cache dtype).
+ * num_tokens = 0 is valid and enqueues nothing.
+ */
+pa_status_t pa_reshape_and_cache(const void* key, const void* value,
+                                 void* key_cache, void* value_cache,
+                                 const int64_t* slot_mapping, int64_t num_tokens,
+                                 int num_kv_heads, int head_size, int block_size,
+                                 int64_t num_blocks, pa_dtype_t kv_dtype, void* stream);
+
+/*
+ * pa_decode -- single-pass paged decode attention.
+ *
+ * Reads each sequence's KV cache from blocks scattered through the pools,
+ * following its block table ("The idea vLLM started from: pages", "What vLLM
+ * Is and Why It Exists"). One workgroup per (sequence, KV head) walks the
+ * whole context, so this suits short contexts; long contexts should use
+ * pa_decode_partitioned.
+ *
+ *   out        [S][Hq][D] of out_dtype (PA_F32 or PA_BF16)
+ *   query      [S][Hq][D] of kv_dtype
+ *   kv_dtype   PA_F32 or PA_BF16, for query, key_cache and value_cache
+ *   num_blocks NB, used to reject out-of-pool table entries on the device
+ *   num_seqs = 0 is valid and enqueues nothing.
+ */
+pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* query,
+                      const void* key_cache, const void* value_cache, pa_dtype_t kv_dtype,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                      float scale, void* stream);
+
+/*
+ * Workspace bytes pa_decode_partitioned needs. With
+ * NP = max(1, ceil(max_context_len / partition_size)) and R = S * Hq * NP,
+ * the workspace holds three float32 arrays, each starting on a 256-byte
+ * boundary: part_max [R], part_sum [R], part_out [R][D], so the size is
+ *     2 * round_up(4 R, 256) + round_up(4 R D, 256).
+ * Returns 0 when an argument is out of range.
+ */
+size_t pa_decode_partitioned_workspace_size(int num_seqs, int num_q_heads, int head_size,
+                                            int max_context_len, int partition_size);
+
+/*
+ * pa_decode_partitioned -- split-context paged decode attention.
+ *
+ * Same inputs and result as pa_decode. Each context is cut into partitions of
+ * partition_size tokens (a multiple of 16); partition p covers tokens
+ * [p * partition_size, min((p + 1) * partition_size, L)). One workgroup per
+ * (sequence, KV head, partition) computes the partition's maximum scaled
+ * logit m_p, sum s_p = sum exp(l_t - m_p) and normalised partial output o_p;
+ * a second kernel combines them:
+ *     M = max_p m_p,  w_p = s_p * exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
+ * (The pages do not describe this variant; it is the standard log-sum-exp
+ * split of softmax and equals the single pass in exact arithmetic.)
+ *
+ *   max_context_len  an upper bound on every context_lens[s], known on the
+ *                    host; it sizes the grid. A longer context gives NaN.
+ *   partition_size   tokens per partition, a positive multiple of 16.
+ *   workspace        device scratch of at least
+ *                    pa_decode_partitioned_workspace_size(...) bytes, 256-byte
+ *                    aligned, laid out as float32 part_max [S][Hq][NP]
+ *                    (natural-log units), part_sum [S][Hq][NP] and part_out
+ *                    [S][Hq][NP][D] (see the size function). Only partitions
+ *                    p < ceil(L / partition_size) are written. Its contents
+ *                    after the call are those partials.
+ */
+pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* query,
+                                  const void* key_cache, const void* value_cache,
+                                  pa_dtype_t kv_dtype, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads,
+                                  int head_size, int block_size, int64_t num_blocks,
+                                  float scale, int max_context_len, int partition_size,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* pa_status_str(pa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

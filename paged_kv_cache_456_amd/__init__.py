@@ -1,0 +1,14 @@
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+The GPU work lives in ``libpa.so`` (hand-written HIP kernels behind the C-ABI
+declared in ``include/pa.h``). This package is its thin Python binding:
+
+    pa_reshape_and_cache   write new tokens' K/V into their cache slots
+    pa_decode              single-pass paged decode attention
+    pa_decode_partitioned  split-context decode with a log-sum-exp reduce
+"""
+from ._lib import (  # noqa: F401
+    PA_BF16, PA_F32, PagedAttentionError, load, pa_decode, pa_decode_partitioned,
+    pa_decode_partitioned_workspace_size, pa_reshape_and_cache, pa_status_str,
+    workspace_partials,
+)

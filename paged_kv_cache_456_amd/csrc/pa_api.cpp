@@ -1,0 +1,246 @@
+// pa_api.cpp -- the C-ABI of the paged decode attention library: argument
+// checks on the host, launch geometry, and the calls into the HIP kernels.
+// Every check runs before anything is enqueued; nothing here allocates,
+// synchronises or keeps state.
+#include <math.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kMaxGroup = 16;          // query heads per KV head handled by one wave
+constexpr int kMaxGridYZ = 65535;      // grid y (sequences) and z (partitions) limits
+constexpr size_t kMaxDecodeLds = 64 * 1024;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool dtype_ok(pa_dtype_t t) { return t == PA_F32 || t == PA_BF16; }
+
+int elem_bytes(pa_dtype_t t) { return t == PA_BF16 ? 2 : 4; }
+
+size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
+
+// Checks shared by both decode entry points. Returns PA_OK when the call may
+// go ahead (num_seqs may still be 0).
+pa_status_t check_decode(const void* out, pa_dtype_t out_dtype, const void* query,
+                         const void* key_cache, const void* value_cache, pa_dtype_t kv_dtype,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                         int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                         float scale) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks < 0)
+        return PA_EINVAL;
+    if (num_q_heads % num_kv_heads != 0)
+        return PA_EINVAL;
+    if (!isfinite(scale))
+        return PA_EINVAL;
+    if (!dtype_ok(kv_dtype) || !dtype_ok(out_dtype))
+        return PA_EUNSUPPORTED;
+    if (block_size != pa::kBlockSize || (head_size != 64 && head_size != 128))
+        return PA_EUNSUPPORTED;
+    if (num_q_heads / num_kv_heads > kMaxGroup || num_seqs > kMaxGridYZ)
+        return PA_EUNSUPPORTED;
+    if (num_seqs == 0)
+        return PA_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+        return PA_EINVAL;
+    if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+        !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return PA_EINVAL;
+    // Byte offsets into the pools are 64-bit; make sure they cannot overflow.
+    const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * pa::kBlockSize * head_size *
+                                elem_bytes(kv_dtype);
+    if (num_blocks > INT64_MAX / block_bytes)
+        return PA_EINVAL;
+    return PA_OK;
+}
+
+pa::DecodeParams make_params(const void* query, const void* key_cache, const void* value_cache,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int num_q_heads, int num_kv_heads,
+                             int64_t num_blocks, float scale) {
+    pa::DecodeParams p{};
+    p.q = query;
+    p.k_cache = key_cache;
+    p.v_cache = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.num_blocks = num_blocks;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_q_heads / num_kv_heads;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return p;
+}
+
+// Waves per workgroup: enough to share the blocks of a partition about four
+// apiece, capped by the workgroup limit and by LDS.
+int choose_waves(int blocks_per_workgroup, int head_size, int group) {
+    int w = (blocks_per_workgroup + 3) / 4;
+    if (w < 1)
+        w = 1;
+    if (w > pa::kMaxWaves)
+        w = pa::kMaxWaves;
+    while (w > 1 && pa::decode_lds_bytes_for(head_size, group, w) > kMaxDecodeLds)
+        --w;
+    return w;
+}
+
+int num_partitions(int max_context_len, int partition_size) {
+    const int64_t np = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+    return np < 1 ? 1 : static_cast<int>(np > INT32_MAX ? INT32_MAX : np);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status_t status) {
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument";
+    case PA_EUNSUPPORTED: return "unsupported configuration";
+    case PA_EWORKSPACE: return "workspace too small";
+    case PA_EHIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                                 void* value_cache, const int64_t* slot_mapping, int64_t num_tokens,
+                                 int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                                 pa_dtype_t kv_dtype, void* stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks < 0)
+        return PA_EINVAL;
+    if (!dtype_ok(kv_dtype) || block_size != pa::kBlockSize || (head_size != 64 && head_size != 128))
+        return PA_EUNSUPPORTED;
+    if (num_tokens > INT32_MAX)
+        return PA_EUNSUPPORTED;
+    if (num_tokens == 0)
+        return PA_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+        return PA_EINVAL;
+    if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+        !aligned(value_cache, 16) || !aligned(slot_mapping, 8))
+        return PA_EINVAL;
+    const int row = head_size * elem_bytes(kv_dtype);
+    const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * pa::kBlockSize * row;
+    if (num_blocks > INT64_MAX / block_bytes)
+        return PA_EINVAL;
+    pa::CacheParams p{};
+    p.key = static_cast<const uint8_t*>(key);
+    p.value = static_cast<const uint8_t*>(value);
+    p.key_cache = static_cast<uint8_t*>(key_cache);
+    p.value_cache = static_cast<uint8_t*>(value_cache);
+    p.slot_mapping = slot_mapping;
+    p.num_slots = num_blocks * pa::kBlockSize;
+    p.num_kv_heads = num_kv_heads;
+    p.row_bytes = row;
+    return from_hip(pa::launch_cache(p, num_tokens, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* query, const void* key_cache,
+                      const void* value_cache, pa_dtype_t kv_dtype, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_size, int block_size,
+                      int64_t num_blocks, float scale, void* stream) {
+    pa_status_t st = check_decode(out, out_dtype, query, key_cache, value_cache, kv_dtype,
+                                  block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                  scale);
+    if (st != PA_OK || num_seqs == 0)
+        return st;
+    pa::DecodeParams p = make_params(query, key_cache, value_cache, block_tables,
+                                     max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads,
+                                     num_blocks, scale);
+    p.out = out;
+    p.partition_blocks = max_blocks_per_seq;
+    p.num_partitions = 1;
+    const int waves = choose_waves(max_blocks_per_seq, head_size, p.group);
+    return from_hip(pa::launch_decode(p, kv_dtype == PA_BF16, head_size, out_dtype == PA_BF16,
+                                      num_seqs, 1, waves, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_partitioned_workspace_size(int num_seqs, int num_q_heads, int head_size,
+                                            int max_context_len, int partition_size) {
+    if (num_seqs < 0 || num_q_heads <= 0 || head_size <= 0 || max_context_len < 0 ||
+        partition_size <= 0)
+        return 0;
+    const unsigned __int128 rows = static_cast<unsigned __int128>(num_seqs) *
+                                   static_cast<unsigned __int128>(num_q_heads) *
+                                   static_cast<unsigned __int128>(num_partitions(max_context_len, partition_size));
+    const unsigned __int128 bytes = 2 * (rows * 4 + 256) + rows * 4 * head_size + 256;
+    if (bytes > static_cast<unsigned __int128>(SIZE_MAX / 2))
+        return 0;
+    const size_t r = static_cast<size_t>(rows);
+    return 2 * align256(r * sizeof(float)) + align256(r * sizeof(float) * head_size);
+}
+
+pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* query,
+                                  const void* key_cache, const void* value_cache,
+                                  pa_dtype_t kv_dtype, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
+                                  int block_size, int64_t num_blocks, float scale,
+                                  int max_context_len, int partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    pa_status_t st = check_decode(out, out_dtype, query, key_cache, value_cache, kv_dtype,
+                                  block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                  scale);
+    if (st != PA_OK)
+        return st;
+    if (max_context_len < 0 || partition_size <= 0 || partition_size % pa::kBlockSize != 0)
+        return PA_EINVAL;
+    const int np = num_partitions(max_context_len, partition_size);
+    if (np > kMaxGridYZ)
+        return PA_EUNSUPPORTED;
+    if (num_seqs == 0)
+        return PA_OK;
+    const size_t need = pa_decode_partitioned_workspace_size(num_seqs, num_q_heads, head_size,
+                                                             max_context_len, partition_size);
+    if (need == 0)
+        return PA_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < need)
+        return PA_EWORKSPACE;
+    if (!aligned(workspace, 256))
+        return PA_EINVAL;
+
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * np;
+    char* ws = static_cast<char*>(workspace);
+    pa::DecodeParams p = make_params(query, key_cache, value_cache, block_tables,
+                                     max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads,
+                                     num_blocks, scale);
+    p.out = nullptr;
+    p.part_max = reinterpret_cast<float*>(ws);
+    p.part_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+    p.part_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+    p.partition_blocks = partition_size / pa::kBlockSize;
+    p.num_partitions = np;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int waves = choose_waves(p.partition_blocks, head_size, p.group);
+    hipError_t e = pa::launch_decode(p, kv_dtype == PA_BF16, head_size, out_dtype == PA_BF16,
+                                     num_seqs, np, waves, s);
+    if (e != hipSuccess)
+        return PA_EHIP;
+
+    pa::ReduceParams r{};
+    r.context_lens = context_lens;
+    r.part_max = p.part_max;
+    r.part_sum = p.part_sum;
+    r.part_out = p.part_out;
+    r.out = out;
+    r.num_q_heads = num_q_heads;
+    r.num_partitions = np;
+    r.partition_size = partition_size;
+    r.max_blocks_per_seq = max_blocks_per_seq;
+    return from_hip(pa::launch_reduce(r, head_size, out_dtype == PA_BF16, num_seqs, s));
+}
+
+}  // extern "C"

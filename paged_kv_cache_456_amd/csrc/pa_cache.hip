@@ -1,0 +1,55 @@
+// pa_cache.hip -- the KV-cache write (reshape_and_cache) for gfx950.
+//
+// Each new token's key and value vectors go into the slot the host chose for
+// it: row slot % 16 of physical block slot / 16, for every KV head. The pages
+// say a request keeps the key/value state of each token it produced and holds
+// only the blocks those tokens fill ("The problem a naive server has" and
+// "The idea vLLM started from: pages" on "What vLLM Is and Why It Exists");
+// the slot numbering is this library's convention.
+//
+// The copy is a bit copy in 16-byte pieces: one workgroup per token, its
+// threads walking the token's Hkv * D elements of K, then of V. Source reads
+// are contiguous; each head's destination row is contiguous.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCacheThreads = 256;
+
+__global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(CacheParams p) {
+    const int64_t t = blockIdx.x;
+    const int64_t slot = p.slot_mapping[t];
+    if (slot < 0 || slot >= p.num_slots)   // padding token, or a slot outside the pool
+        return;
+    const int64_t blk = slot / kBlockSize;
+    const int64_t off = slot % kBlockSize;
+    const int cph = p.row_bytes / 16;              // 16-byte pieces per head row
+    const int chunks = p.num_kv_heads * cph;       // pieces per token per tensor
+    for (int c = threadIdx.x; c < 2 * chunks; c += blockDim.x) {
+        const bool is_v = c >= chunks;
+        const int cc = is_v ? c - chunks : c;
+        const int h = cc / cph;
+        const int w = cc - h * cph;
+        const uint8_t* src = (is_v ? p.value : p.key) + (t * chunks + cc) * 16;
+        uint8_t* dst = (is_v ? p.value_cache : p.key_cache) +
+                       ((blk * p.num_kv_heads + h) * kBlockSize + off) * p.row_bytes + w * 16;
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_cache(const CacheParams& p, int64_t num_tokens, hipStream_t stream) {
+    const int pieces = 2 * p.num_kv_heads * (p.row_bytes / 16);
+    int threads = ((pieces + kWave - 1) / kWave) * kWave;
+    if (threads > kCacheThreads)
+        threads = kCacheThreads;
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(static_cast<unsigned>(num_tokens)),
+                       dim3(threads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -177,10 +177,19 @@ def _normal(shape, dtype, gen, device) -> torch.Tensor:
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dtype)
 
 
-def make_workload(name: str, device="cpu", *, poison: bool = True, table_pad: int | str = "poison",
+def custom_spec(lengths: List[int], num_q_heads: int, num_kv_heads: int, head_size: int,
+                dtype: torch.dtype, new_tokens_per_seq: int = 1, index: int = 100) -> WorkloadSpec:
+    """A workload of given context lengths and shapes, with a pool twice the blocks needed."""
+    return WorkloadSpec(index, f"custom{index}", num_seqs=len(lengths), num_q_heads=num_q_heads,
+                        num_kv_heads=num_kv_heads, head_size=head_size, dtype=dtype,
+                        lengths="fixed:" + ",".join(str(int(v)) for v in lengths), pool="twice",
+                        new_tokens_per_seq=new_tokens_per_seq)
+
+
+def make_workload(name, device="cpu", *, poison: bool = True, table_pad: int | str = "poison",
                   num_blocks: Optional[int] = None, lengths: Optional[List[int]] = None,
                   seed_offset: int = 0) -> Workload:
-    """Build the named workload.
+    """Build the named workload (or the one a WorkloadSpec describes).
 
     device      where the value tensors are drawn and kept (the random stream
                 depends on the device, the layout does not).
@@ -192,7 +201,7 @@ def make_workload(name: str, device="cpu", *, poison: bool = True, table_pad: in
     lengths     override the context lengths (same count as num_seqs).
     seed_offset added to both seeds, to draw independent replicas.
     """
-    spec = SPECS[name]
+    spec = name if isinstance(name, WorkloadSpec) else SPECS[name]
     B = BLOCK_SIZE
     elem_bytes = torch.tensor([], dtype=spec.dtype).element_size()
     lay_rng = np.random.default_rng(_LAYOUT_SEED_BASE + spec.index + 7919 * seed_offset)

@@ -1,0 +1,134 @@
+"""The C-ABI boundary on the CPU: libpa.so loads, exports every function that
+include/pa.h declares, and its host-side checks return the documented status
+codes before anything is enqueued. No kernel is launched here: every call
+below either fails a host check or has nothing to do."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_456_amd as pa
+from paged_kv_cache_456_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+EINVAL, EUNSUP, EWS, OK = _lib.PA_EINVAL, _lib.PA_EUNSUPPORTED, _lib.PA_EWORKSPACE, _lib.PA_OK
+
+# Fake, aligned, never-dereferenced addresses: every call that receives them
+# fails a host-side check first.
+P = 0x10000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w ]+\*?\s*(pa_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    assert pa.pa_status_str(0) == "ok"
+    assert pa.pa_status_str(3) == "workspace too small"
+    assert pa.pa_status_str(99) == "unknown status"
+
+
+def cache_call(lib, **kw):
+    a = dict(key=P, value=P, key_cache=P, value_cache=P, slots=P, T=4, Hkv=4, D=64, B=16, NB=32,
+             dt=0)
+    a.update(kw)
+    return lib.pa_reshape_and_cache(a["key"], a["value"], a["key_cache"], a["value_cache"],
+                                    a["slots"], a["T"], a["Hkv"], a["D"], a["B"], a["NB"], a["dt"],
+                                    None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(T=0), OK), (dict(T=0, key=0), OK),
+    (dict(T=-1), EINVAL), (dict(Hkv=0), EINVAL), (dict(NB=-1), EINVAL),
+    (dict(B=8), EUNSUP), (dict(D=96), EUNSUP), (dict(dt=5), EUNSUP),
+    (dict(key=0), EINVAL), (dict(slots=0), EINVAL), (dict(value_cache=P + 4), EINVAL),
+    (dict(slots=P + 4), EINVAL), (dict(T=1 << 33), EUNSUP), (dict(NB=1 << 62), EINVAL),
+])
+def test_cache_checks(lib, kw, expect):
+    assert cache_call(lib, **kw) == expect
+
+
+def decode_args(**kw):
+    a = dict(out=P, out_dt=0, q=P, kc=P, vc=P, kv_dt=0, bt=P, MB=3, cl=P, S=4, Hq=4, Hkv=4, D=64,
+             B=16, NB=32, scale=0.125)
+    a.update(kw)
+    return a
+
+
+def decode_call(lib, **kw):
+    a = decode_args(**kw)
+    return lib.pa_decode(a["out"], a["out_dt"], a["q"], a["kc"], a["vc"], a["kv_dt"], a["bt"],
+                         a["MB"], a["cl"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
+                         a["scale"], None)
+
+
+DECODE_CASES = [
+    (dict(S=0), OK), (dict(S=0, out=0, q=0), OK),
+    (dict(S=-1), EINVAL), (dict(Hq=6, Hkv=4), EINVAL), (dict(MB=0), EINVAL), (dict(NB=-2), EINVAL),
+    (dict(scale=math.nan), EINVAL), (dict(scale=math.inf), EINVAL),
+    (dict(B=32), EUNSUP), (dict(D=256), EUNSUP), (dict(kv_dt=3), EUNSUP), (dict(out_dt=2), EUNSUP),
+    (dict(Hq=34, Hkv=2), EUNSUP), (dict(S=70000), EUNSUP),
+    (dict(out=0), EINVAL), (dict(bt=0), EINVAL), (dict(cl=0), EINVAL), (dict(q=P + 8), EINVAL),
+    (dict(bt=P + 2), EINVAL), (dict(NB=1 << 60), EINVAL),
+]
+
+
+@pytest.mark.parametrize("kw,expect", DECODE_CASES)
+def test_decode_checks(lib, kw, expect):
+    assert decode_call(lib, **kw) == expect
+
+
+def part_call(lib, max_ctx=37, psize=32, ws=P, ws_bytes=1 << 20, **kw):
+    a = decode_args(**kw)
+    return lib.pa_decode_partitioned(a["out"], a["out_dt"], a["q"], a["kc"], a["vc"], a["kv_dt"],
+                                     a["bt"], a["MB"], a["cl"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                                     a["B"], a["NB"], a["scale"], max_ctx, psize, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", DECODE_CASES)
+def test_partitioned_shares_decode_checks(lib, kw, expect):
+    assert part_call(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(psize=24), EINVAL), (dict(psize=0), EINVAL), (dict(max_ctx=-1), EINVAL),
+    (dict(ws=0), EWS), (dict(ws_bytes=100), EWS), (dict(ws=P + 16), EINVAL),
+    (dict(max_ctx=16 * 70000, psize=16), EUNSUP),
+    (dict(S=0, ws=0, ws_bytes=0), OK),
+])
+def test_partitioned_checks(lib, kw, expect):
+    assert part_call(lib, **kw) == expect
+
+
+def test_workspace_size_formula(lib):
+    a256 = lambda n: (n + 255) // 256 * 256
+    for S, Hq, D, L, Ps in [(64, 32, 128, 4096, 256), (8, 64, 128, 32768, 512), (4, 4, 64, 37, 32),
+                            (3, 2, 64, 0, 16), (1, 1, 64, 16, 16)]:
+        R = S * Hq * max(1, -(-L // Ps))
+        assert pa.pa_decode_partitioned_workspace_size(S, Hq, D, L, Ps) == 2 * a256(4 * R) + a256(4 * R * D)
+    assert pa.pa_decode_partitioned_workspace_size(-1, 4, 64, 10, 16) == 0
+    assert pa.pa_decode_partitioned_workspace_size(1, 4, 64, 10, 0) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 64)
+    with pytest.raises(ValueError):
+        pa.pa_reshape_and_cache(x, x, x.view(1, 1, 1, 64), x.view(1, 1, 1, 64),
+                                torch.zeros(1, dtype=torch.int64))

@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Bar: the cache write is bit-exact; attention outputs are within max abs error
+2e-3 (bf16 KV) or 1e-5 (fp32 KV) of the oracle, on fp32 outputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_456_amd as pa
+from paged_kv_cache_456_amd import workloads as wl
+from harness import TOL, check_scatter, device_inputs, gpu_step, max_abs_err, oracle_step
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load()
+    return torch.device("cuda")
+
+
+def _report(tag, err, tol):
+    print(f"[{tag}] max abs err {err:.3e} (tol {tol:.0e})", flush=True)
+    assert err <= tol, f"{tag}: {err} > {tol}"
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_tiny_fp32():
+    w = wl.make_workload("tiny_fp32", device="cuda")
+    r = oracle_step(w)
+    for psize in (None, 16, 32, 48):
+        g = gpu_step(w, partition_size=psize)
+        check_scatter(w, g, r)
+        _report(f"tiny_fp32 P={psize}", max_abs_err(g.out, r.out), TOL[torch.float32])
+
+
+@pytest.mark.parametrize("name,psizes,seqs", [
+    ("llama8b_gqa_bf16", (None, 256, 512), None),
+    ("prefix_shared_bf16", (None, 512), None),
+    ("long_context_bf16", (512,), [0, 5]),
+])
+def test_workload(name, psizes, seqs):
+    w = wl.make_workload(name, device="cuda")
+    r = oracle_step(w, seqs=seqs)
+    idx = torch.as_tensor(r.seqs, device="cuda")
+    for psize in psizes:
+        g = gpu_step(w, partition_size=psize)
+        check_scatter(w, g, r)
+        _report(f"{name} P={psize}", max_abs_err(g.out[idx], r.out), TOL[torch.bfloat16])
+        assert torch.isfinite(g.out).all()
+
+
+@pytest.mark.big
+def test_large_batch_sampled():
+    """256 sequences, pool of ~60% of HBM; the oracle checks a sample of sequences."""
+    free, _ = torch.cuda.mem_get_info()
+    spec = wl.SPECS["large_batch_bf16"]
+    per_block = 2 * spec.num_kv_heads * 16 * spec.head_size * 2
+    nb = int(min(0.6 * wl.HBM_BYTES, 0.85 * free) // per_block)
+    w = wl.make_workload("large_batch_bf16", device="cuda", poison=False, num_blocks=nb)
+    seqs = [0, 77, 254]
+    r = oracle_step(w, seqs=seqs, partition_size=512)
+    g = gpu_step(w, partition_size=512, in_place=True)
+    check_scatter(w, g, r, full_pool=False)
+    _report("large_batch P=512", max_abs_err(g.out[torch.as_tensor(seqs, device="cuda")], r.out),
+            TOL[torch.bfloat16])
+
+
+# ---------------------------------------------------------------- shapes
+
+MATRIX = [
+    (torch.float32, 64, 4, 1), (torch.float32, 64, 8, 2), (torch.float32, 128, 4, 4),
+    (torch.float32, 128, 2, 8),
+    (torch.bfloat16, 64, 2, 1), (torch.bfloat16, 64, 4, 3), (torch.bfloat16, 64, 2, 8),
+    (torch.bfloat16, 128, 3, 1), (torch.bfloat16, 128, 4, 2), (torch.bfloat16, 128, 2, 6),
+    (torch.bfloat16, 128, 1, 16), (torch.bfloat16, 64, 1, 16),
+]
+
+
+@pytest.mark.parametrize("dtype,D,Hkv,G", MATRIX, ids=lambda v: str(v).replace("torch.", ""))
+def test_shape_matrix(dtype, D, Hkv, G):
+    lengths = [1, 2, 15, 16, 17, 31, 64, 100, 257, 700]
+    spec = wl.custom_spec(lengths, Hkv * G, Hkv, D, dtype, index=200 + D + 3 * G + Hkv)
+    w = wl.make_workload(spec, device="cuda")
+    r = oracle_step(w)
+    for psize in (None, 16, 64, 256):
+        g = gpu_step(w, partition_size=psize)
+        check_scatter(w, g, r)
+        _report(f"{dtype} D={D} Hkv={Hkv} G={G} P={psize}", max_abs_err(g.out, r.out), TOL[dtype])
+
+
+def test_long_single_pass_many_blocks():
+    """More than 64 blocks per wave in the single pass (the table is re-read per 64)."""
+    spec = wl.custom_spec([8192, 5000, 3], 8, 2, 128, torch.bfloat16, index=301)
+    w = wl.make_workload(spec, device="cuda")
+    r = oracle_step(w)
+    g = gpu_step(w)
+    _report("single pass 8192", max_abs_err(g.out, r.out), TOL[torch.bfloat16])
+
+
+# ---------------------------------------------------------------- partials, out dtype
+
+def test_partials_match_oracle():
+    spec = wl.custom_spec([5, 16, 300, 1000], 8, 2, 128, torch.bfloat16, index=302)
+    w = wl.make_workload(spec, device="cuda")
+    P = 128
+    r = oracle_step(w, partition_size=P)
+    g = gpu_step(w, partition_size=P)
+    pm, ps, po = pa.workspace_partials(g.workspace, w.num_seqs, spec.num_q_heads, spec.head_size,
+                                       w.max_context_len, P)
+    om, os_, oo = r.part
+    for s, L in enumerate(w.context_lens):
+        n = -(-int(L) // P)
+        gm, gs, go = pm[s, :, :n].double().cpu().numpy(), ps[s, :, :n].double().cpu().numpy(), \
+            po[s, :, :n].double().cpu().numpy()
+        assert np.max(np.abs(gm - om[s, :, :n])) < 1e-4
+        assert np.max(np.abs(gs / os_[s, :, :n] - 1)) < 1e-4
+        assert np.max(np.abs(go - oo[s, :, :n])) < TOL[torch.bfloat16]
+
+
+def test_bf16_output():
+    w = wl.make_workload("llama8b_gqa_bf16", device="cuda")
+    r = oracle_step(w)
+    for psize in (None, 256):
+        g = gpu_step(w, partition_size=psize, out_dtype=torch.bfloat16)
+        err = np.abs(g.out.double().cpu().numpy() - r.out) - 2.0 ** -8 * np.abs(r.out)
+        _report(f"bf16 out P={psize} (beyond half a bf16 ulp)", float(err.max()), TOL[torch.bfloat16])
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_block_permutation_bit_identical():
+    """Moving blocks elsewhere in the pool leaves the output bit-identical."""
+    w = wl.make_workload("llama8b_gqa_bf16", device="cuda")
+    base = gpu_step(w)
+    base_p = gpu_step(w, partition_size=256)
+    perm = torch.randperm(w.num_blocks, generator=torch.Generator().manual_seed(5))
+    inv = perm.to("cuda")
+    kc2 = torch.empty_like(w.key_cache)
+    vc2 = torch.empty_like(w.value_cache)
+    kc2[inv] = w.key_cache
+    vc2[inv] = w.value_cache
+    bt2 = perm[torch.from_numpy(w.block_tables).long()].int().numpy()
+    slots = w.slot_mapping
+    slots2 = np.where(slots >= 0, perm[torch.from_numpy(slots // 16)].numpy() * 16 + slots % 16, -1)
+    w2 = wl.Workload(**{**w.__dict__, "key_cache": kc2, "value_cache": vc2,
+                        "block_tables": bt2.astype(np.int32), "slot_mapping": slots2})
+    moved = gpu_step(w2)
+    moved_p = gpu_step(w2, partition_size=256)
+    assert torch.equal(base.out, moved.out)
+    assert torch.equal(base_p.out, moved_p.out)
+
+
+def test_prefix_unshared_bit_identical():
+    """Sequences sharing prefix blocks give the same bits as with private copies, and
+    the copy-on-write parent block is never written."""
+    w = wl.make_workload("prefix_shared_bf16", device="cuda")
+    shared = gpu_step(w, partition_size=512)
+    parent_k = w.key_cache[w.cow_parent].clone()
+    assert torch.equal(_bits16(shared.key_cache[w.cow_parent]), _bits16(parent_k))
+    # Give every sequence its own copy of the prefix.
+    nshared = len(w.shared_blocks)
+    S = w.num_seqs
+    extra = S * nshared
+    kc = torch.cat([w.key_cache, w.key_cache[torch.as_tensor(w.shared_blocks, device="cuda")].repeat(S, 1, 1, 1)])
+    vc = torch.cat([w.value_cache, w.value_cache[torch.as_tensor(w.shared_blocks, device="cuda")].repeat(S, 1, 1, 1)])
+    bt = w.block_tables.copy()
+    for s in range(S):
+        bt[s, :nshared] = w.num_blocks + s * nshared + np.arange(nshared)
+    w2 = wl.Workload(**{**w.__dict__, "key_cache": kc, "value_cache": vc, "block_tables": bt,
+                        "num_blocks": w.num_blocks + extra})
+    private = gpu_step(w2, partition_size=512)
+    assert torch.equal(shared.out, private.out)
+
+
+def _bits16(t):
+    return t.view(torch.int16)
+
+
+def test_repeat_bitwise():
+    w = wl.make_workload("llama8b_gqa_bf16", device="cuda")
+    a = gpu_step(w, partition_size=256)
+    b = gpu_step(w, partition_size=256)
+    assert torch.equal(a.out, b.out)
+
+
+def test_partitioned_close_to_single_pass():
+    w = wl.make_workload("llama8b_gqa_bf16", device="cuda")
+    single = gpu_step(w)
+    for psize in (16, 256, 4096):
+        part = gpu_step(w, partition_size=psize)
+        assert (part.out - single.out).abs().max().item() < 1e-5
+
+
+def test_single_token_returns_v_exactly():
+    for dtype in (torch.float32, torch.bfloat16):
+        spec = wl.custom_spec([1, 1, 1], 8, 2, 128, dtype, index=303)
+        w = wl.make_workload(spec, device="cuda")
+        for psize in (None, 16):
+            g = gpu_step(w, partition_size=psize)
+            G = 4
+            v = w.value.float()                      # the token just written, [S, Hkv, D]
+            ref = v.repeat_interleave(G, dim=1)
+            assert torch.equal(g.out, ref)
+
+
+def test_constant_values_give_one():
+    w = wl.make_workload("llama8b_gqa_bf16", device="cuda")
+    w.value_cache.copy_(torch.where(torch.isnan(w.value_cache), w.value_cache,
+                                    torch.ones_like(w.value_cache)))
+    w.value.fill_(1.0)
+    for psize in (None, 256):
+        g = gpu_step(w, partition_size=psize)
+        assert (g.out - 1).abs().max().item() < 1e-6
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_edge_lengths_and_bad_tables():
+    spec = wl.custom_spec([0, 1, 40, 33, 20], 8, 2, 64, torch.bfloat16, index=304)
+    w = wl.make_workload(spec, device="cuda", table_pad=-1)
+    r = oracle_step(w, seqs=[0, 1, 2])
+    bt, cl, _ = device_inputs(w)
+    bt_bad = bt.clone()
+    bt_bad[3, 1] = w.num_blocks + 3            # out-of-pool id inside sequence 3's context
+    cl_bad = cl.clone()
+    cl_bad[4] = bt.shape[1] * 16 + 1           # longer than its table
+    for psize in (None, 16):
+        g = gpu_step(w, partition_size=psize, block_tables=bt_bad, context_lens=cl_bad)
+        _report(f"edge P={psize}", max_abs_err(g.out[:3], r.out), TOL[torch.bfloat16])
+        assert torch.equal(g.out[0], torch.zeros_like(g.out[0]))        # L = 0
+        assert torch.isnan(g.out[3]).all() and torch.isnan(g.out[4]).all()
+
+
+def test_context_beyond_max_context_len_is_nan():
+    spec = wl.custom_spec([40, 70], 4, 2, 64, torch.bfloat16, index=305)
+    w = wl.make_workload(spec, device="cuda")
+    g = gpu_step(w, partition_size=16, max_context_len=48)
+    assert torch.isfinite(g.out[0]).all() and torch.isnan(g.out[1]).all()
+
+
+def test_scatter_skips_padding_and_out_of_pool_slots():
+    spec = wl.custom_spec([20, 30], 4, 2, 64, torch.bfloat16, index=306)
+    w = wl.make_workload(spec, device="cuda")
+    kc, vc = w.key_cache.clone(), w.value_cache.clone()
+    slots = torch.tensor([-1, w.num_blocks * 16 + 5], dtype=torch.int64, device="cuda")
+    pa.pa_reshape_and_cache(w.key, w.value, kc, vc, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits16(kc), _bits16(w.key_cache))
+    assert torch.equal(_bits16(vc), _bits16(w.value_cache))
+
+
+def test_empty_batch_and_side_stream():
+    w = wl.make_workload("tiny_fp32", device="cuda")
+    r = oracle_step(w)
+    bt, cl, slots = device_inputs(w)
+    out = torch.empty_like(w.query)
+    pa.pa_decode(out[:0], w.query[:0], w.key_cache, w.value_cache, bt[:0], cl[:0], w.scale)
+    side = torch.cuda.Stream()
+    kc, vc = w.key_cache.clone(), w.value_cache.clone()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        pa.pa_reshape_and_cache(w.key, w.value, kc, vc, slots)
+        pa.pa_decode(out, w.query, kc, vc, bt, cl, w.scale)
+    side.synchronize()
+    _report("side stream", max_abs_err(out, r.out), TOL[torch.float32])
