@@ -103,14 +103,13 @@ def main() -> int:
     Hkv = spec.num_kv_heads
     kv_bytes = base.kv_bytes()
     mcl = base.max_context_len
-    ws_bytes = pa.pa_decode_partitioned_workspace_size(S, Hq, D, mcl, psize)
     inputs = []
     for w in reps:
         inputs.append(dict(
             w=w, bt=torch.from_numpy(w.block_tables).to(dev), cl=torch.from_numpy(w.context_lens).to(dev),
             slots=torch.from_numpy(w.slot_mapping).to(dev),
             out=torch.empty((S, Hq, D), dtype=torch.float32, device=dev),
-            ws=torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)))
+            ws=pa.decode_workspace(S, Hq, D, mcl, psize, device=dev)))
     torch.cuda.synchronize()
     log(f"[bench] {args.workload}: S={S} Hq={Hq} Hkv={Hkv} D={D} sum(L)={int(base.context_lens.sum())} "
         f"KV bytes/step={kv_bytes / 1e6:.1f} MB, replicas={args.replicas}, kernel={args.kernel}, P={psize}")

@@ -147,10 +147,14 @@ size_t pa_decode_partitioned_workspace_size(int num_seqs, int num_q_heads, int h
  * [p * partition_size, min((p + 1) * partition_size, L)). One workgroup per
  * (sequence, KV head, partition) computes the partition's maximum scaled
  * logit m_p, sum s_p = sum exp(l_t - m_p) and normalised partial output o_p;
- * a second kernel combines them:
+ * a second kernel combines the partitions of each (sequence, KV head), in
+ * partition order:
  *     M = max_p m_p,  w_p = s_p * exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
  * (The pages do not describe this variant; it is the standard log-sum-exp
  * split of softmax and equals the single pass in exact arithmetic.)
+ * A sequence whose context fits one partition gets its output row written
+ * directly, and when every context fits one partition (NP = 1) the second
+ * kernel is not launched.
  *
  *   max_context_len  an upper bound on every context_lens[s], known on the
  *                    host; it sizes the grid. A longer context gives NaN.
@@ -159,9 +163,11 @@ size_t pa_decode_partitioned_workspace_size(int num_seqs, int num_q_heads, int h
  *                    pa_decode_partitioned_workspace_size(...) bytes, 256-byte
  *                    aligned, laid out as float32 part_max [S][Hq][NP]
  *                    (natural-log units), part_sum [S][Hq][NP] and part_out
- *                    [S][Hq][NP][D] (see the size function). Only partitions
- *                    p < ceil(L / partition_size) are written. Its contents
- *                    after the call are those partials.
+ *                    [S][Hq][NP][D] (see the size function). Its contents
+ *                    before the call do not matter. After the call, for every
+ *                    sequence with more than one partition, the entries of
+ *                    partitions p < ceil(L / partition_size) hold the
+ *                    partials; all other entries are unspecified.
  */
 pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* query,
                                   const void* key_cache, const void* value_cache,

@@ -8,7 +8,7 @@ declared in ``include/pa.h``). This package is its thin Python binding:
     pa_decode_partitioned  split-context decode with a log-sum-exp reduce
 """
 from ._lib import (  # noqa: F401
-    PA_BF16, PA_F32, PagedAttentionError, load, pa_decode, pa_decode_partitioned,
-    pa_decode_partitioned_workspace_size, pa_reshape_and_cache, pa_status_str,
-    workspace_partials,
+    PA_BF16, PA_F32, PagedAttentionError, decode_workspace, load, pa_decode,
+    pa_decode_partitioned, pa_decode_partitioned_workspace_size, pa_reshape_and_cache,
+    pa_status_str, workspace_partials,
 )

@@ -155,7 +155,7 @@ def pa_decode_partitioned(out: torch.Tensor, query: torch.Tensor, key_cache: tor
                           partition_size: int, workspace: torch.Tensor,
                           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """Split-context paged decode attention. workspace is a uint8 GPU tensor of at least
-    pa_decode_partitioned_workspace_size(...) bytes."""
+    pa_decode_partitioned_workspace_size(...) bytes (decode_workspace() makes one)."""
     S, Hq, Hkv, D, B, NB, MB = _decode_common(out, query, key_cache, value_cache, block_tables,
                                               context_lens)
     _dev(workspace)
@@ -168,6 +168,16 @@ def pa_decode_partitioned(out: torch.Tensor, query: torch.Tensor, key_cache: tor
                                       _stream(query, stream))
     _check(rc, "pa_decode_partitioned")
     return out
+
+
+def decode_workspace(num_seqs: int, num_q_heads: int, head_size: int, max_context_len: int,
+                     partition_size: int, device=None) -> torch.Tensor:
+    """An uninitialised uint8 GPU workspace of the size pa_decode_partitioned needs."""
+    n = pa_decode_partitioned_workspace_size(num_seqs, num_q_heads, head_size, max_context_len,
+                                             partition_size)
+    if n == 0:
+        raise ValueError("workspace size out of range")
+    return torch.empty(n, dtype=torch.uint8, device=device if device is not None else "cuda")
 
 
 def workspace_partials(workspace: torch.Tensor, num_seqs: int, num_q_heads: int, head_size: int,

@@ -79,15 +79,18 @@ pa::DecodeParams make_params(const void* query, const void* key_cache, const voi
     return p;
 }
 
-// Waves per workgroup: enough to share the blocks of a partition about four
-// apiece, capped by the workgroup limit and by LDS.
-int choose_waves(int blocks_per_workgroup, int head_size, int group) {
-    int w = (blocks_per_workgroup + 3) / 4;
+// Waves per workgroup: enough for one round to cover the blocks a workgroup
+// owns (each wave takes decode_bpw blocks per round), capped by `max_waves`
+// and by LDS. Partitioned launches use small (4-wave) workgroups so that two
+// or more fit on a CU; the single pass uses up to 8 waves per sequence.
+int choose_waves(int blocks_per_workgroup, int kv_bytes, int head_size, int group, int max_waves) {
+    const int bpw = pa::decode_bpw(kv_bytes, head_size, pa::decode_gmax(group));
+    int w = (blocks_per_workgroup + bpw - 1) / bpw;
     if (w < 1)
         w = 1;
-    if (w > pa::kMaxWaves)
-        w = pa::kMaxWaves;
-    while (w > 1 && pa::decode_lds_bytes_for(head_size, group, w) > kMaxDecodeLds)
+    if (w > max_waves)
+        w = max_waves;
+    while (w > 1 && pa::decode_lds_bytes(kv_bytes, head_size, group, w) > kMaxDecodeLds)
         --w;
     return w;
 }
@@ -162,7 +165,10 @@ pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* query, const 
     p.out = out;
     p.partition_blocks = max_blocks_per_seq;
     p.num_partitions = 1;
-    const int waves = choose_waves(max_blocks_per_seq, head_size, p.group);
+    p.num_seqs = num_seqs;
+    p.persistent = 0;
+    const int waves = choose_waves(max_blocks_per_seq, elem_bytes(kv_dtype), head_size, p.group,
+                                   pa::kMaxWaves);
     return from_hip(pa::launch_decode(p, kv_dtype == PA_BF16, head_size, out_dtype == PA_BF16,
                                       num_seqs, 1, waves, static_cast<hipStream_t>(stream)));
 }
@@ -217,18 +223,23 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
     pa::DecodeParams p = make_params(query, key_cache, value_cache, block_tables,
                                      max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads,
                                      num_blocks, scale);
-    p.out = nullptr;
+    p.out = out;
     p.part_max = reinterpret_cast<float*>(ws);
     p.part_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
     p.part_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
     p.partition_blocks = partition_size / pa::kBlockSize;
     p.num_partitions = np;
+    p.num_seqs = num_seqs;
+    p.persistent = num_seqs <= pa::kMaxPersistentSeqs && num_kv_heads <= pa::kMaxPersistentKvHeads;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int waves = choose_waves(p.partition_blocks, head_size, p.group);
+    const int waves = choose_waves(p.partition_blocks, elem_bytes(kv_dtype), head_size, p.group,
+                                   pa::kPartWaves);
     hipError_t e = pa::launch_decode(p, kv_dtype == PA_BF16, head_size, out_dtype == PA_BF16,
                                      num_seqs, np, waves, s);
     if (e != hipSuccess)
         return PA_EHIP;
+    if (np == 1)
+        return PA_OK;    // every context fits one partition: no partials to combine
 
     pa::ReduceParams r{};
     r.context_lens = context_lens;
@@ -236,10 +247,13 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
     r.part_sum = p.part_sum;
     r.part_out = p.part_out;
     r.out = out;
-    r.num_q_heads = num_q_heads;
-    r.num_partitions = np;
-    r.partition_size = partition_size;
+    r.num_blocks = num_blocks;
     r.max_blocks_per_seq = max_blocks_per_seq;
+    r.num_q_heads = num_q_heads;
+    r.num_kv_heads = num_kv_heads;
+    r.group = p.group;
+    r.num_partitions = np;
+    r.partition_blocks = p.partition_blocks;
     return from_hip(pa::launch_reduce(r, head_size, out_dtype == PA_BF16, num_seqs, s));
 }
 

@@ -21,22 +21,24 @@ constexpr int kCacheThreads = 256;
 
 __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(CacheParams p) {
     const int64_t t = blockIdx.x;
-    const int64_t slot = p.slot_mapping[t];
-    if (slot < 0 || slot >= p.num_slots)   // padding token, or a slot outside the pool
-        return;
-    const int64_t blk = slot / kBlockSize;
-    const int64_t off = slot % kBlockSize;
     const int cph = p.row_bytes / 16;              // 16-byte pieces per head row
     const int chunks = p.num_kv_heads * cph;       // pieces per token per tensor
+    // The slot is needed only for the stores: its load and the source loads
+    // are in flight together.
+    const int64_t slot = p.slot_mapping[t];
     for (int c = threadIdx.x; c < 2 * chunks; c += blockDim.x) {
         const bool is_v = c >= chunks;
         const int cc = is_v ? c - chunks : c;
+        const u32x4 piece = *reinterpret_cast<const u32x4*>((is_v ? p.value : p.key) + (t * chunks + cc) * 16);
+        if (slot < 0 || slot >= p.num_slots)   // padding token, or a slot outside the pool
+            return;
+        const int64_t blk = slot / kBlockSize;
+        const int64_t off = slot % kBlockSize;
         const int h = cc / cph;
         const int w = cc - h * cph;
-        const uint8_t* src = (is_v ? p.value : p.key) + (t * chunks + cc) * 16;
         uint8_t* dst = (is_v ? p.value_cache : p.key_cache) +
                        ((blk * p.num_kv_heads + h) * kBlockSize + off) * p.row_bytes + w * 16;
-        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+        *reinterpret_cast<u32x4*>(dst) = piece;
     }
 }
 

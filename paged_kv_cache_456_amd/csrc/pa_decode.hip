@@ -1,4 +1,4 @@
-// pa_decode.hip -- paged decode attention kernels for gfx950 (CDNA4).
+// pa_decode.hip -- paged decode attention kernel for gfx950 (CDNA4).
 //
 // What is computed: for each sequence, its one new query token attends over
 // a KV cache held in 16-token blocks scattered through a shared pool and
@@ -8,30 +8,41 @@
 // scaled dot-product softmax attention (the pages print no formula).
 //
 // Work decomposition. One workgroup per (KV head, sequence, context
-// partition); its waves take the partition's blocks round-robin. Every query
-// head of the group that shares the KV head is handled by the same wave, so
-// each K/V byte is read from HBM once per step.
+// partition); the single-pass entry point is the case of one partition that
+// spans the whole context. Every query head of the group that shares the KV
+// head is handled by the same wave, so each K/V byte is read from HBM once
+// per step. The partition's blocks are dealt out in rounds: in each round,
+// wave w takes BPW consecutive blocks.
 //
-// Per block (16 tokens x D of one KV head, one contiguous tile):
-//   * the physical block id comes from a per-wave register that holds the
-//     wave's whole slice of the block table (one vector load per 64 blocks,
-//     v_readlane per block): the table is resolved once per wavefront;
+// Per round, per wave:
+//   * physical block ids come from a per-wave register holding the wave's
+//     slice of the block table (one vector load per 64 entries, v_readlane
+//     per block), so each table entry is resolved once per wavefront;
+//   * the K and V tiles of all BPW blocks (16 tokens x D of one KV head, a
+//     contiguous run in the pool) are requested together, before any of them
+//     is used, and the next round's tiles are requested while this round is
+//     computed (K as soon as Q^T K has consumed the K registers, V after P.V);
 //   * K is loaded so that lane l holds token l%16, 16-byte chunks l/16+4c of
-//     its row, which is the B-operand layout of a 16x16 MFMA. Q^T K for the
-//     whole head group is one MFMA chain (bf16: v_mfma_f32_16x16x32_bf16,
-//     fp32: v_mfma_f32_16x16x4_f32), heads as rows, tokens as columns;
+//     its row: the B-operand layout of a 16x16 MFMA. Q^T K for the whole head
+//     group is an MFMA chain (bf16: v_mfma_f32_16x16x32_bf16, fp32:
+//     v_mfma_f32_16x16x4_f32), heads as rows, tokens as columns;
 //   * softmax statistics are kept online (running max and sum, base-2
-//     exponent with scale*log2(e) folded in); the block max is a 16-lane DPP
-//     row reduction;
+//     exponent with scale*log2(e) folded in); the round max is an in-lane max
+//     over the BPW blocks followed by a 16-lane DPP row reduction;
 //   * V is loaded fully coalesced (consecutive lanes read consecutive 16-byte
-//     chunks); P.V runs on the VALU in fp32 with P in fp32, because P in bf16
-//     would cost about 2e-3 of accuracy. P moves from the MFMA layout to the V
-//     layout through 1 KB of LDS per wave;
-//   * the next block's K and V are prefetched into registers while the
-//     current block is computed.
-// Waves then merge their (max, sum, output) through LDS in a fixed order, so
-// results depend only on logical token positions, never on where the blocks
-// sit in the pool.
+//     chunks); P.V runs on the VALU in fp32 with P in fp32 (P rounded to bf16
+//     would cost about 2e-3 of accuracy). P moves from the MFMA layout to the
+//     V layout through a small per-wave LDS tile.
+// The waves then merge their (max, sum, output) through LDS in a fixed order.
+//
+// Split contexts. A sequence with a single partition writes its output row
+// directly. Otherwise each partition writes its (max, sum, normalised
+// output) to the workspace and a second, small kernel combines the
+// partitions of each (sequence, KV head) with log-sum-exp weights, in
+// partition order. Every reduction runs in an order fixed by logical token
+// positions, so results never depend on where the blocks sit in the pool.
+#include <algorithm>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -39,7 +50,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -82,6 +92,18 @@ __device__ __forceinline__ u32x4 ld16(const char* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// KV tiles are read once per step: stream them past the caches.
+__device__ __forceinline__ u32x4 ld16_stream(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Make this wave's LDS writes visible to its own later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // fp32 -> bf16, round to nearest even, NaN kept NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     uint32_t u = __float_as_uint(x);
@@ -107,7 +129,6 @@ struct Ops;
 
 template <>
 struct Ops<BF16> {
-    static constexpr int kEpc = 8;   // elements per 16-byte chunk
     __device__ static __forceinline__ void to_f32(const u32x4& c, float (&f)[8]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -124,7 +145,6 @@ struct Ops<BF16> {
 
 template <>
 struct Ops<F32> {
-    static constexpr int kEpc = 4;
     __device__ static __forceinline__ void to_f32(const u32x4& c, float (&f)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -152,48 +172,40 @@ struct Geometry {
     static_assert(kCh >= 4 && kCh <= kWave, "row must span 4..64 chunks");
 };
 
-template <typename KV, int D>
-struct Tile {
-    u32x4 k[Geometry<KV, D>::kNq];
-    u32x4 v[Geometry<KV, D>::kNv];
-};
-
-// Dynamic LDS layout per workgroup of nw waves:
-//   p_lds  [nw][16][16]   P of the current block, [token][head]
-//   red_m  [nw][GP]       per-wave running max (base-2 units), GP = GMAX rounded up to 4
-//   red_s  [nw][GP]       per-wave sum of exponentials
-//   red_o  [nw][GMAX][D]  per-wave unnormalised output
-// (GMAX rounded up to 4 keeps red_o 16-byte aligned.)
-template <int GMAX>
-constexpr int padded_group() { return (GMAX + 3) & ~3; }
-
-template <int GMAX, int D>
-__host__ __device__ constexpr size_t decode_lds_bytes(int nw) {
-    return sizeof(float) * static_cast<size_t>(nw) * (256 + 2 * padded_group<GMAX>() + GMAX * D);
+// A context that cannot be read -- longer than its block table or than the
+// partitions of the launch, or a non-empty context in an empty pool -- gets
+// an all-NaN output row. Both kernels apply the same rule.
+__device__ __forceinline__ bool context_unreadable(int L, int max_blocks_per_seq, int num_partitions,
+                                                   int partition_blocks, int64_t num_blocks) {
+    const int64_t cap = min(static_cast<int64_t>(max_blocks_per_seq),
+                            static_cast<int64_t>(num_partitions) * partition_blocks) * kBlockSize;
+    return L < 0 || static_cast<int64_t>(L) > cap || (L > 0 && num_blocks <= 0);
 }
 
+// One work item: the partition `part` of KV head `kvh` of sequence `s`
+// (context length L), computed by the whole workgroup. Writes the output row
+// directly when the context has a single partition, else the partition's
+// partials. All arguments are wave-uniform.
 template <typename KV, int D, int GMAX, typename OUT>
-__global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeParams p) {
+__device__ __forceinline__ void process_item(const DecodeParams& p, float* smem, int kvh, int s,
+                                             int part, int L) {
     using Gm = Geometry<KV, D>;
     using Op = Ops<KV>;
     constexpr int NQ = Gm::kNq, NV = Gm::kNv, CH = Gm::kCh, TPL = Gm::kTpl, EPC = Gm::kEpc;
     constexpr int ROW = Gm::kRow, TILE = Gm::kTile;
+    constexpr int BPW = decode_bpw(KV::kBytes, D, GMAX);
+    constexpr int GP = decode_pstride(GMAX);
+    constexpr int RPB = kWave / BPW;              // rounds covered by one batch of table entries
 
-    extern __shared__ float smem[];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nw = blockDim.x / kWave;
-    const int kvh = blockIdx.x;
-    const int s = blockIdx.y;
-    const int part = blockIdx.z;
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads, G = p.group;
 
-    const int L = p.context_lens[s];
-    const bool bad_len = L < 0 || static_cast<int64_t>(L) >
-                                      static_cast<int64_t>(p.max_blocks_per_seq) * kBlockSize;
+    const bool bad_len = context_unreadable(L, p.max_blocks_per_seq, p.num_partitions,
+                                            p.partition_blocks, p.num_blocks);
     if (bad_len || L == 0) {
-        // Partitioned mode leaves these rows to the reduce kernel.
-        if (p.out != nullptr && part == 0) {
+        if (part == 0) {
             const float fill = bad_len ? __builtin_nanf("") : 0.0f;
             for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
                 const int h = idx / D, d = idx - (idx / D) * D;
@@ -203,13 +215,15 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeP
         return;
     }
     const int nblk = (L + kBlockSize - 1) / kBlockSize;
+    const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
     const int pb0 = part * p.partition_blocks;
     if (pb0 >= nblk)
         return;
     const int pb1 = min(pb0 + p.partition_blocks, nblk);
     const int tok_end = min(pb1 * kBlockSize, L);
-    const int nb = pb1 - pb0;
-    const int nbw = nb > wave ? (nb - wave + nw - 1) / nw : 0;   // this wave's blocks
+    const int per_round = nw * BPW;
+    const int rounds = (pb1 - pb0 + per_round - 1) / per_round;
+    const int wb0 = pb0 + wave * BPW;            // this wave's first block of round 0
 
     const int g = lane >> 4;       // MFMA lane group: output rows 4g..4g+3
     const int r16 = lane & 15;     // MFMA row/column index: A-operand head, token column
@@ -232,6 +246,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeP
     const int64_t blk_stride = (int64_t)Hkv * TILE;
     const int koff = r16 * ROW + g * 16;            // + 64 c
     const int voff = vrow * ROW + vchunk * 16;      // + TPL * ROW * c
+    const int64_t tbl = (int64_t)s * p.max_blocks_per_seq;
 
     float m[4], lsum[4];
     float o[GMAX][EPC];
@@ -246,119 +261,171 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeP
         for (int e = 0; e < EPC; ++e)
             o[h][e] = 0.0f;
 
-    float* p_lds = smem + wave * 256;
+    float* p_lds = smem + wave * (BPW * kBlockSize * GP);
     bool poisoned = false;
 
-    auto load_tile = [&](int phys, Tile<KV, D>& t) {
-        const char* kb = kbase + (int64_t)phys * blk_stride + koff;
-        const char* vb = vbase + (int64_t)phys * blk_stride + voff;
-#pragma unroll
-        for (int c = 0; c < NQ; ++c)
-            t.k[c] = ld16(kb + 64 * c);
-#pragma unroll
-        for (int c = 0; c < NV; ++c)
-            t.v[c] = ld16(vb + TPL * ROW * c);
+    // Table entries of rounds [r0, r0 + RPB): lane i holds block b = i % BPW of
+    // round r0 + i / BPW. An entry inside the context that lies outside the
+    // pool marks the wave poisoned (its output becomes NaN) and is replaced by
+    // block 0, so that every load stays inside the pool.
+    int phys_l = 0;
+    int batch_r0 = 0;
+    auto load_entries = [&](int r0) {
+        const int jb = wb0 + (r0 + lane / BPW) * per_round + lane % BPW;
+        const bool mine = jb < pb1;
+        const int e = mine ? p.block_tables[tbl + jb] : 0;
+        const bool bad = e < 0 || static_cast<int64_t>(e) >= p.num_blocks;
+        phys_l = bad ? 0 : e;
+        batch_r0 = r0;
+        if (__ballot(bad) != 0)
+            poisoned = true;
+    };
+    auto block_of = [&](int r, int b) { return wb0 + r * per_round + b; };   // logical block
+    // Slots of a round past the partition's end re-read the partition's last
+    // tile (one that is read anyway, so the extra reads hit in cache) and are
+    // masked out afterwards. Every slot is loaded, so no load sits under a
+    // branch and the compiler can wait for each tile precisely.
+    int last_phys = p.block_tables[tbl + pb1 - 1];
+    if (last_phys < 0 || static_cast<int64_t>(last_phys) >= p.num_blocks) {
+        poisoned = true;
+        last_phys = 0;
+    }
+    auto phys_of = [&](int r, int b) {
+        const int v = __builtin_amdgcn_readlane(phys_l, (r - batch_r0) * BPW + b);
+        return block_of(r, b) < pb1 ? v : last_phys;
     };
 
-    auto process = [&](const Tile<KV, D>& t, int blk) {
-        // logits[head 4g+j][token r16]
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 kt[BPW][NQ], vt[BPW][NV];
+    auto issue_k = [&](int r) {
 #pragma unroll
-        for (int c = 0; c < NQ; ++c)
-            acc = Op::qk(qa[c], t.k[c], acc);
-        const int valid = min(kBlockSize, tok_end - blk * kBlockSize);
-        const bool tvalid = r16 < valid;
-        float pexp[4], alpha[4];
+        for (int b = 0; b < BPW; ++b) {
+            const char* kb = kbase + (int64_t)phys_of(r, b) * blk_stride + koff;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float x = tvalid ? acc[j] * p.scale_log2 : -INFINITY;
-            const float mn = fmaxf(m[j], row_max16(x));
-            alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
-            pexp[j] = __builtin_amdgcn_exp2f(x - mn);
-            lsum[j] = lsum[j] * alpha[j] + pexp[j];
-            m[j] = mn;
+            for (int c = 0; c < NQ; ++c)
+                kt[b][c] = ld16_stream(kb + 64 * c);
         }
-        *reinterpret_cast<f32x4*>(p_lds + r16 * 16 + 4 * g) = f32x4{pexp[0], pexp[1], pexp[2], pexp[3]};
-        float al[GMAX];
+    };
+    auto issue_v = [&](int r) {
 #pragma unroll
-        for (int h = 0; h < GMAX; ++h)
-            al[h] = readlane_f(alpha[h & 3], 16 * (h >> 2));
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int b = 0; b < BPW; ++b) {
+            const char* vb = vbase + (int64_t)phys_of(r, b) * blk_stride + voff;
 #pragma unroll
-        for (int h = 0; h < GMAX; ++h)
+            for (int c = 0; c < NV; ++c)
+                vt[b][c] = ld16_stream(vb + TPL * ROW * c);
+        }
+    };
+
+    // One round: Q^T K, online softmax and P.V over this wave's BPW slots. The
+    // following round's K is requested as soon as the K registers are consumed
+    // and its V once P.V is done.
+    auto round = [&](int r) {
+        const int nvb = min(BPW, max(0, pb1 - block_of(r, 0)));   // this wave's blocks this round
+        // ---- logits of the round's slots: heads 4g+j, token column r16
+        f32x4 acc[BPW];
 #pragma unroll
-            for (int e = 0; e < EPC; ++e)
-                o[h][e] *= al[h];
+        for (int b = 0; b < BPW; ++b) {
+            acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int c = 0; c < NV; ++c) {
-            const int tr = vrow + TPL * c;
-            float pv[GMAX];
-            if constexpr (GMAX >= 4) {
+            for (int c = 0; c < NQ; ++c)
+                acc[b] = Op::qk(qa[c], kt[b][c], acc[b]);
+        }
+        if (r + 1 < rounds) {
+            if (r + 1 - batch_r0 >= RPB)
+                load_entries(r + 1);
+            issue_k(r + 1);
+        }
+        if (nvb > 0) {
+            // ---- online softmax over the round
+            float x[BPW][4];
+            float alpha[4];
 #pragma unroll
-                for (int h4 = 0; h4 < GMAX; h4 += 4) {
-                    const f32x4 q4 = *reinterpret_cast<const f32x4*>(p_lds + tr * 16 + h4);
-                    pv[h4] = q4[0];
-                    pv[h4 + 1] = q4[1];
-                    pv[h4 + 2] = q4[2];
-                    pv[h4 + 3] = q4[3];
+            for (int j = 0; j < 4; ++j) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int b = 0; b < BPW; ++b) {
+                    const bool tvalid = block_of(r, b) * kBlockSize + r16 < tok_end;
+                    x[b][j] = tvalid ? acc[b][j] * p.scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, x[b][j]);
                 }
-            } else {
+                const float mn = fmaxf(m[j], row_max16(mx));
+                alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
+                float ps = 0.0f;
 #pragma unroll
-                for (int h = 0; h < GMAX; ++h)
-                    pv[h] = p_lds[tr * 16 + h];
+                for (int b = 0; b < BPW; ++b) {
+                    x[b][j] = __builtin_amdgcn_exp2f(x[b][j] - mn);
+                    ps += x[b][j];
+                }
+                lsum[j] = lsum[j] * alpha[j] + ps;
+                m[j] = mn;
             }
-            float vf[EPC];
-            Op::to_f32(t.v[c], vf);
-            if (valid < kBlockSize && tr >= valid) {
-                // Tail rows may hold anything (even NaN): drop them, do not scale them by 0.
+            if (4 * g < GP) {
 #pragma unroll
-                for (int e = 0; e < EPC; ++e)
-                    vf[e] = 0.0f;
+                for (int b = 0; b < BPW; ++b)
+                    *reinterpret_cast<f32x4*>(p_lds + (b * kBlockSize + r16) * GP + 4 * g) =
+                        f32x4{x[b][0], x[b][1], x[b][2], x[b][3]};
             }
+            float al[GMAX];
+#pragma unroll
+            for (int h = 0; h < GMAX; ++h)
+                al[h] = readlane_f(alpha[h & 3], 16 * (h >> 2));
+            wave_lds_sync();
 #pragma unroll
             for (int h = 0; h < GMAX; ++h)
 #pragma unroll
                 for (int e = 0; e < EPC; ++e)
-                    o[h][e] = fmaf(pv[h], vf[e], o[h][e]);
+                    o[h][e] *= al[h];
+            // ---- P.V
+#pragma unroll
+            for (int b = 0; b < BPW; ++b) {
+                // Valid rows of the slot: 16 for a full block, fewer for the
+                // context's last block, none (<= 0) for a slot past the end.
+                const int tvalid = tok_end - block_of(r, b) * kBlockSize;
+#pragma unroll
+                for (int c = 0; c < NV; ++c) {
+                    const int tr = vrow + TPL * c;
+                    const float* prow = p_lds + (b * kBlockSize + tr) * GP;
+                    float pv[GMAX];
+                    if constexpr (GMAX >= 4) {
+#pragma unroll
+                        for (int h4 = 0; h4 < GMAX; h4 += 4) {
+                            const f32x4 q4 = *reinterpret_cast<const f32x4*>(prow + h4);
+                            pv[h4] = q4[0];
+                            pv[h4 + 1] = q4[1];
+                            pv[h4 + 2] = q4[2];
+                            pv[h4 + 3] = q4[3];
+                        }
+                    } else {
+#pragma unroll
+                        for (int h = 0; h < GMAX; ++h)
+                            pv[h] = prow[h];
+                    }
+                    float vf[EPC];
+                    Op::to_f32(vt[b][c], vf);
+                    if (tvalid < kBlockSize && tr >= tvalid) {
+                        // Tail rows may hold anything (even NaN): drop them, do not scale by 0.
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e)
+                            vf[e] = 0.0f;
+                    }
+#pragma unroll
+                    for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e)
+                            o[h][e] = fmaf(pv[h], vf[e], o[h][e]);
+                }
+            }
+            wave_lds_sync();
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (r + 1 < rounds)
+            issue_v(r + 1);
     };
 
-    const int64_t tbl = (int64_t)s * p.max_blocks_per_seq + pb0 + wave;
-    for (int b0 = 0; b0 < nbw && !poisoned; b0 += kWave) {
-        const int nbatch = min(kWave, nbw - b0);
-        // Resolve this wave's next (up to) 64 block-table entries at once.
-        int phys_l = 0;
-        if (lane < nbatch)
-            phys_l = p.block_tables[tbl + (int64_t)(b0 + lane) * nw];
-        const bool bad = lane < nbatch && (phys_l < 0 || static_cast<int64_t>(phys_l) >= p.num_blocks);
-        if (__ballot(bad) != 0) {
-            poisoned = true;
-            break;
-        }
-        // Two register tiles in ping-pong: block i+1 is in flight while block i is computed.
-        const int jb = pb0 + wave + b0 * nw;      // logical index of the batch's first block
-        Tile<KV, D> ta, tb;
-        load_tile(__builtin_amdgcn_readlane(phys_l, 0), ta);
-        int i = 0;
-        for (; i + 2 < nbatch; i += 2) {
-            load_tile(__builtin_amdgcn_readlane(phys_l, i + 1), tb);
-            process(ta, jb + i * nw);
-            load_tile(__builtin_amdgcn_readlane(phys_l, i + 2), ta);
-            process(tb, jb + (i + 1) * nw);
-        }
-        if (i + 1 < nbatch) {
-            load_tile(__builtin_amdgcn_readlane(phys_l, i + 1), tb);
-            process(ta, jb + i * nw);
-            process(tb, jb + (i + 1) * nw);
-        } else {
-            process(ta, jb + i * nw);
-        }
-    }
+    load_entries(0);
+    issue_k(0);
+    issue_v(0);
+#pragma nounroll
+    for (int r = 0; r < rounds; ++r)
+        round(r);
 
     // Wave totals: sums over the 16 token columns, outputs over the token rows.
     float srow[4];
@@ -385,8 +452,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeP
                 o[h][e] = __builtin_nanf("");
     }
 
-    constexpr int GP = padded_group<GMAX>();
-    float* red_m = smem + nw * 256;
+    float* red_m = smem + nw * (BPW * kBlockSize * GP);
     float* red_s = red_m + nw * GP;
     float* red_o = red_s + nw * GP;
     if (r16 == 0) {
@@ -410,7 +476,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeP
     }
     __syncthreads();
 
-    // Merge the waves in a fixed order and write this workgroup's result.
+    // Merge the waves in a fixed order.
+    const bool split = nparts > 1;
     for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
         const int h = idx / D;
         const int d = idx - h * D;
@@ -424,7 +491,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeP
             acc = fmaf(red_o[(w * GMAX + h) * D + d], f, acc);
         }
         const int64_t row = (int64_t)s * Hq + (int64_t)kvh * G + h;
-        if (p.out != nullptr) {
+        if (!split) {
             store_out<OUT>(p.out, row * D + d, acc / S);
         } else {
             const int64_t pi = row * p.num_partitions + part;
@@ -437,79 +504,215 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeP
     }
 }
 
-// Log-sum-exp combination of the partitions of one (sequence, query head).
-template <int D, typename OUT>
-__global__ __launch_bounds__(kWave) void lse_reduce_kernel(ReduceParams p) {
-    constexpr int DPL = D / kWave;   // output elements per lane (1 or 2)
-    const int h = blockIdx.x;
-    const int s = blockIdx.y;
-    const int lane = threadIdx.x;
-    const int Hq = p.num_q_heads, NP = p.num_partitions;
-    const int L = p.context_lens[s];
-    const int64_t orow = ((int64_t)s * Hq + h) * D;
-    const bool bad = L < 0 ||
-                     static_cast<int64_t>(L) > static_cast<int64_t>(p.max_blocks_per_seq) * kBlockSize ||
-                     static_cast<int64_t>(L) > static_cast<int64_t>(NP) * p.partition_size;
-    if (bad || L == 0) {
-        const float fill = bad ? __builtin_nanf("") : 0.0f;
+// Work slots of a sequence in the persistent schedule: its partitions, or a
+// single slot (which writes the zero or NaN row) when there is nothing to read.
+__device__ __forceinline__ int sequence_slots(int L, const DecodeParams& p) {
+    if (L == 0 || context_unreadable(L, p.max_blocks_per_seq, p.num_partitions, p.partition_blocks,
+                                     p.num_blocks))
+        return 1;
+    const int nblk = (L + kBlockSize - 1) / kBlockSize;
+    return (nblk + p.partition_blocks - 1) / p.partition_blocks;
+}
+
+// Grid mode (one workgroup per (KV head, sequence, partition), the single
+// pass included) or persistent mode: a grid no larger than what the GPU holds
+// at once, where workgroup w takes the items w, w + grid, w + 2 grid, ... of
+// the list of (sequence, partition, KV head) items that actually exist. The
+// list is built from context_lens in LDS, so no workgroup is spent on the
+// empty partitions of short sequences.
+template <typename KV, int D, int GMAX, typename OUT>
+__global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeParams p) {
+    extern __shared__ float smem[];
+    process_item<KV, D, GMAX, OUT>(p, smem, blockIdx.x, blockIdx.y, blockIdx.z,
+                                   p.context_lens[blockIdx.y]);
+}
+
+// Waves per SIMD the persistent kernel is register-allocated for: three
+// 4-wave workgroups per CU for head groups up to 4, two for larger ones.
+template <typename KV, int D, int GMAX>
+constexpr int persistent_waves_per_simd() {
+    return (GMAX <= 4 && D * KV::kBytes <= 256) ? 3 : 2;
+}
+
+template <typename KV, int D, int GMAX, typename OUT>
+__global__ __launch_bounds__(kPartWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(persistent_waves_per_simd<KV, D, GMAX>())))
+void paged_decode_persistent_kernel(DecodeParams p) {
+    extern __shared__ float smem[];
+    const int nw = blockDim.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int S = p.num_seqs, Hkv = p.num_kv_heads;
+    int* lens = reinterpret_cast<int*>(smem + decode_lds_floats(KV::kBytes, D, p.group, nw));
+    int* first_slot = lens + S;                 // [S + 1], exclusive prefix sum of slots
+    int* list = first_slot + S + 1;             // [kItemListCap][2]: sequence, part << 8 | kvh
+    for (int i = threadIdx.x; i < S; i += blockDim.x)
+        lens[i] = p.context_lens[i];
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        int carry = 0;
+        for (int c0 = 0; c0 < S; c0 += kWave) {
+            const int i = c0 + lane;
+            const int v = i < S ? sequence_slots(lens[i], p) : 0;
+            int incl = v;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k)
-            store_out<OUT>(p.out, orow + lane * DPL + k, fill);
-        return;
-    }
-    const int np = (L + p.partition_size - 1) / p.partition_size;
-    const int64_t base = ((int64_t)s * Hq + h) * NP;
-    float mx = -INFINITY;
-    for (int i = lane; i < np; i += kWave)
-        mx = fmaxf(mx, p.part_max[base + i]);
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-    float acc[DPL];
-#pragma unroll
-    for (int k = 0; k < DPL; ++k)
-        acc[k] = 0.0f;
-    float wsum = 0.0f;
-    for (int i = 0; i < np; ++i) {
-        const float w = p.part_sum[base + i] * __builtin_amdgcn_exp2f((p.part_max[base + i] - mx) * kLog2e);
-        wsum += w;
-        const float* po = p.part_out + (base + i) * D + lane * DPL;
-        if constexpr (DPL == 2) {
-            const f32x2 v = *reinterpret_cast<const f32x2*>(po);
-            acc[0] = fmaf(w, v[0], acc[0]);
-            acc[1] = fmaf(w, v[1], acc[1]);
-        } else {
-            acc[0] = fmaf(w, po[0], acc[0]);
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int t = __shfl_up(incl, off, kWave);
+                if (lane >= off)
+                    incl += t;
+            }
+            if (i < S)
+                first_slot[i] = carry + incl - v;
+            carry += __shfl(incl, kWave - 1, kWave);
         }
+        if (lane == 0)
+            first_slot[S] = carry;
     }
+    __syncthreads();
+    const int64_t items = static_cast<int64_t>(first_slot[S]) * Hkv;
+    for (int64_t k0 = 0; blockIdx.x + k0 * gridDim.x < items; k0 += kItemListCap) {
+        for (int k = threadIdx.x; k < kItemListCap; k += blockDim.x) {
+            const int64_t it = blockIdx.x + (k0 + k) * gridDim.x;
+            int seq = -1, pk = 0;
+            if (it < items) {
+                const int slot = static_cast<int>(it / Hkv);
+                const int kvh = static_cast<int>(it - static_cast<int64_t>(slot) * Hkv);
+                int lo = 0, hi = S;                 // last sequence whose first slot <= slot
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (first_slot[mid] <= slot)
+                        lo = mid;
+                    else
+                        hi = mid;
+                }
+                seq = lo;
+                pk = ((slot - first_slot[lo]) << 8) | kvh;
+            }
+            list[2 * k] = seq;
+            list[2 * k + 1] = pk;
+        }
+        __syncthreads();
+        for (int k = 0; k < kItemListCap; ++k) {
+            const int seq = __builtin_amdgcn_readfirstlane(list[2 * k]);
+            if (seq < 0)
+                break;
+            const int pk = __builtin_amdgcn_readfirstlane(list[2 * k + 1]);
+            process_item<KV, D, GMAX, OUT>(p, smem, pk & 0xFF, seq, pk >> 8,
+                                           __builtin_amdgcn_readfirstlane(lens[seq]));
+            __syncthreads();                        // the item's LDS is free again
+        }
+        __syncthreads();                            // every thread is done with this list
+    }
+}
+
+// Log-sum-exp combination of the partitions of every (sequence, KV head)
+// whose context spans more than one partition: one workgroup per pair, one
+// wave per query head at a time. The wave loads the head's partition maxima
+// and sums lane-parallel, reduces them to the weights
+//     w_p = s_p exp(m_p - M) / sum_q s_q exp(m_q - M),  M = max_p m_p,
+// stages the weights in LDS, and accumulates sum_p w_p o_p over the partition
+// outputs with independent loads. All reductions run in a fixed order.
+template <int D, typename OUT>
+__global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams p) {
+    constexpr int DPL = D / kWave;              // output elements per lane
+    __shared__ float wts[kReduceThreads / kWave][kWave];
+    const int kvh = blockIdx.x;
+    const int s = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int G = p.group, Hq = p.num_q_heads, NP = p.num_partitions;
+    const int L = p.context_lens[s];
+    if (L == 0 || context_unreadable(L, p.max_blocks_per_seq, NP, p.partition_blocks, p.num_blocks))
+        return;                                // the partition kernel wrote this row
+    const int nblk = (L + kBlockSize - 1) / kBlockSize;
+    const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+    if (nparts <= 1)
+        return;                                // written directly by its only partition
+    for (int h = wave; h < G; h += nw) {
+        const int64_t row = (int64_t)s * Hq + (int64_t)kvh * G + h;
+        const int64_t base = row * NP;
+        float mx = -INFINITY;
+        for (int i = lane; i < nparts; i += kWave)
+            mx = fmaxf(mx, p.part_max[base + i]);
 #pragma unroll
-    for (int k = 0; k < DPL; ++k)
-        store_out<OUT>(p.out, orow + lane * DPL + k, acc[k] / wsum);
+        for (int off = 1; off < kWave; off <<= 1)
+            mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+        float tot = 0.0f;
+        for (int i = lane; i < nparts; i += kWave)
+            tot += p.part_sum[base + i] * __builtin_amdgcn_exp2f((p.part_max[base + i] - mx) * kLog2e);
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1)
+            tot += __shfl_xor(tot, off, kWave);
+        float acc[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+            acc[e] = 0.0f;
+        for (int c0 = 0; c0 < nparts; c0 += kWave) {
+            const int i = c0 + lane;
+            wts[wave][lane] = i < nparts ? p.part_sum[base + i] *
+                                               __builtin_amdgcn_exp2f((p.part_max[base + i] - mx) * kLog2e)
+                                         : 0.0f;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int n = min(kWave, nparts - c0);
+            const float* po = p.part_out + (base + c0) * D + lane;
+#pragma unroll 8
+            for (int j = 0; j < n; ++j) {
+                const float w = wts[wave][j];
+#pragma unroll
+                for (int e = 0; e < DPL; ++e)
+                    acc[e] = fmaf(w, po[j * D + e * kWave], acc[e]);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+            store_out<OUT>(p.out, row * D + lane + e * kWave, acc[e] / tot);
+    }
 }
 
 template <typename KV, int D, int GMAX, typename OUT>
 hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, int grid_partitions, int waves,
                            hipStream_t stream) {
-    const size_t lds = decode_lds_bytes<GMAX, D>(waves);
-    hipLaunchKernelGGL((paged_decode_kernel<KV, D, GMAX, OUT>),
-                       dim3(p.num_kv_heads, num_seqs, grid_partitions), dim3(waves * kWave), lds,
-                       stream, p);
+    if (!p.persistent) {
+        const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, waves);
+        hipLaunchKernelGGL((paged_decode_kernel<KV, D, GMAX, OUT>),
+                           dim3(p.num_kv_heads, num_seqs, grid_partitions), dim3(waves * kWave), lds,
+                           stream, p);
+        return hipGetLastError();
+    }
+    const auto kernel = paged_decode_persistent_kernel<KV, D, GMAX, OUT>;
+    // Persistent: as many workgroups as the GPU keeps resident at once (never
+    // more than there can be items).
+    const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, waves) + persistent_lds_bytes(num_seqs);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, waves * kWave, lds);
+    if (e != hipSuccess)
+        return e;
+    const int64_t bound = static_cast<int64_t>(num_seqs) * p.num_kv_heads * grid_partitions;
+    const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(bound, static_cast<int64_t>(cus) *
+                                                                         std::max(per_cu, 1)));
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(waves * kWave), lds, stream, p);
     return hipGetLastError();
 }
 
 template <typename KV, int D, typename OUT>
 hipError_t launch_decode_g(const DecodeParams& p, int num_seqs, int grid_partitions, int waves,
                            hipStream_t stream) {
-    const int G = p.group;
-    if (G <= 1)
-        return launch_decode_t<KV, D, 1, OUT>(p, num_seqs, grid_partitions, waves, stream);
-    if (G <= 2)
-        return launch_decode_t<KV, D, 2, OUT>(p, num_seqs, grid_partitions, waves, stream);
-    if (G <= 4)
-        return launch_decode_t<KV, D, 4, OUT>(p, num_seqs, grid_partitions, waves, stream);
-    if (G <= 8)
-        return launch_decode_t<KV, D, 8, OUT>(p, num_seqs, grid_partitions, waves, stream);
-    return launch_decode_t<KV, D, 16, OUT>(p, num_seqs, grid_partitions, waves, stream);
+    switch (decode_gmax(p.group)) {
+    case 1: return launch_decode_t<KV, D, 1, OUT>(p, num_seqs, grid_partitions, waves, stream);
+    case 2: return launch_decode_t<KV, D, 2, OUT>(p, num_seqs, grid_partitions, waves, stream);
+    case 4: return launch_decode_t<KV, D, 4, OUT>(p, num_seqs, grid_partitions, waves, stream);
+    case 8: return launch_decode_t<KV, D, 8, OUT>(p, num_seqs, grid_partitions, waves, stream);
+    default: return launch_decode_t<KV, D, 16, OUT>(p, num_seqs, grid_partitions, waves, stream);
+    }
 }
 
 template <typename KV, int D>
@@ -521,10 +724,21 @@ hipError_t launch_decode_o(const DecodeParams& p, int out_bf16, int num_seqs, in
 
 }  // namespace
 
-size_t decode_lds_bytes_for(int head_size, int group, int waves) {
-    const int gmax = group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : group <= 8 ? 8 : 16;
-    const int gp = (gmax + 3) & ~3;
-    return sizeof(float) * static_cast<size_t>(waves) * (256 + 2 * gp + gmax * head_size);
+hipError_t launch_reduce(const ReduceParams& p, int head_size, int out_bf16, int num_seqs,
+                         hipStream_t stream) {
+    const dim3 grid(p.num_kv_heads, num_seqs);
+    if (head_size == 64) {
+        if (out_bf16)
+            hipLaunchKernelGGL((lse_reduce_kernel<64, BF16>), grid, dim3(kReduceThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((lse_reduce_kernel<64, F32>), grid, dim3(kReduceThreads), 0, stream, p);
+    } else {
+        if (out_bf16)
+            hipLaunchKernelGGL((lse_reduce_kernel<128, BF16>), grid, dim3(kReduceThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((lse_reduce_kernel<128, F32>), grid, dim3(kReduceThreads), 0, stream, p);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams& p, int kv_bf16, int head_size, int out_bf16,
@@ -537,23 +751,6 @@ hipError_t launch_decode(const DecodeParams& p, int kv_bf16, int head_size, int 
     return head_size == 64
                ? launch_decode_o<F32, 64>(p, out_bf16, num_seqs, grid_partitions, waves, stream)
                : launch_decode_o<F32, 128>(p, out_bf16, num_seqs, grid_partitions, waves, stream);
-}
-
-hipError_t launch_reduce(const ReduceParams& p, int head_size, int out_bf16, int num_seqs,
-                         hipStream_t stream) {
-    const dim3 grid(p.num_q_heads, num_seqs);
-    if (head_size == 64) {
-        if (out_bf16)
-            hipLaunchKernelGGL((lse_reduce_kernel<64, BF16>), grid, dim3(kWave), 0, stream, p);
-        else
-            hipLaunchKernelGGL((lse_reduce_kernel<64, F32>), grid, dim3(kWave), 0, stream, p);
-    } else {
-        if (out_bf16)
-            hipLaunchKernelGGL((lse_reduce_kernel<128, BF16>), grid, dim3(kWave), 0, stream, p);
-        else
-            hipLaunchKernelGGL((lse_reduce_kernel<128, F32>), grid, dim3(kWave), 0, stream, p);
-    }
-    return hipGetLastError();
 }
 
 }  // namespace pa

@@ -9,7 +9,9 @@ namespace pa {
 
 constexpr int kBlockSize = 16;   // tokens per KV block
 constexpr int kWave = 64;        // CDNA wavefront width
-constexpr int kMaxWaves = 8;     // waves per decode workgroup
+constexpr int kMaxWaves = 8;     // waves per decode workgroup (single pass)
+constexpr int kPartWaves = 4;    // waves per decode workgroup (partitioned)
+constexpr int kReduceThreads = 256;
 
 // Element tags for the KV dtype.
 struct BF16 {
@@ -26,7 +28,7 @@ struct DecodeParams {
     const void* v_cache;           // [NB][Hkv][16][D]
     const int32_t* block_tables;   // [S][MB]
     const int32_t* context_lens;   // [S]
-    void* out;                     // [S][Hq][D]   (single pass) or nullptr
+    void* out;                     // [S][Hq][D]
     float* part_max;               // [S][Hq][NP]  (partitioned) or nullptr
     float* part_sum;               // [S][Hq][NP]
     float* part_out;               // [S][Hq][NP][D]
@@ -37,19 +39,24 @@ struct DecodeParams {
     int group;                     // Hq / Hkv
     int partition_blocks;          // blocks per partition (single pass: >= MB)
     int num_partitions;            // NP, the workspace stride
+    int num_seqs;
+    int persistent;                // 1: persistent schedule over the items that exist
     float scale_log2;              // scale * log2(e)
 };
 
 struct ReduceParams {
     const int32_t* context_lens;
-    const float* part_max;
-    const float* part_sum;
-    const float* part_out;
-    void* out;
-    int num_q_heads;
-    int num_partitions;
-    int partition_size;
+    const float* part_max;         // [S][Hq][NP], natural-log units
+    const float* part_sum;         // [S][Hq][NP]
+    const float* part_out;         // [S][Hq][NP][D]
+    void* out;                     // [S][Hq][D]
+    int64_t num_blocks;
     int max_blocks_per_seq;
+    int num_q_heads;
+    int num_kv_heads;
+    int group;
+    int num_partitions;
+    int partition_blocks;
 };
 
 struct CacheParams {
@@ -63,14 +70,55 @@ struct CacheParams {
     int row_bytes;                 // D * element bytes
 };
 
+// Query heads per KV head that a decode kernel instance is compiled for:
+// the group size rounded up to 1, 2, 4, 8 or 16.
+constexpr int decode_gmax(int group) {
+    return group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : group <= 8 ? 8 : 16;
+}
+
+// Blocks each wave loads per round. A round's K and V tiles sit in registers
+// together (8 * D * elem_bytes / 64 bytes of VGPRs per lane per block); two
+// blocks of bf16 D = 128 keep 16 KB in flight per wave. Wide rows and large
+// head groups take one.
+constexpr int decode_bpw(int elem_bytes, int head_size, int gmax) {
+    return (gmax > 8 || head_size * elem_bytes > 256) ? 1 : 2;
+}
+
+// Row stride, in floats, of the per-wave softmax-weight tile in LDS.
+constexpr int decode_pstride(int gmax) { return gmax < 4 ? 4 : gmax; }
+
+// Floats of decode LDS per workgroup of `waves` waves (layout below).
+constexpr size_t decode_lds_floats(int elem_bytes, int head_size, int group, int waves) {
+    return static_cast<size_t>(waves) *
+           (static_cast<size_t>(decode_bpw(elem_bytes, head_size, decode_gmax(group))) * 16 *
+                decode_pstride(decode_gmax(group)) +
+            2 * decode_pstride(decode_gmax(group)) +
+            static_cast<size_t>(decode_gmax(group)) * head_size);
+}
+
+// Dynamic LDS bytes of a decode workgroup of `waves` waves:
+//   p    [waves][bpw * 16][pstride]  softmax weights of the current round
+//   m, s [waves][pstride]            per-wave running max and sum
+//   o    [waves][gmax][D]            per-wave unnormalised output
+constexpr size_t decode_lds_bytes(int elem_bytes, int head_size, int group, int waves) {
+    return sizeof(float) * decode_lds_floats(elem_bytes, head_size, group, waves);
+}
+
+// Persistent schedule: items handled per pass over the list, and the largest
+// batch (context lengths and their prefix sums are kept in LDS).
+constexpr int kItemListCap = 256;
+constexpr int kMaxPersistentSeqs = 4096;
+constexpr int kMaxPersistentKvHeads = 256;
+// Extra LDS of the persistent schedule: lens [S], first_slot [S + 1], list [cap][2].
+constexpr size_t persistent_lds_bytes(int num_seqs) {
+    return sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1 + 2 * kItemListCap);
+}
+
 // Launchers (pa_decode.hip, pa_cache.hip). kv: 0 = fp32, 1 = bf16.
 hipError_t launch_decode(const DecodeParams& p, int kv_bf16, int head_size, int out_bf16,
                          int num_seqs, int grid_partitions, int waves, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, int head_size, int out_bf16, int num_seqs,
                          hipStream_t stream);
 hipError_t launch_cache(const CacheParams& p, int64_t num_tokens, hipStream_t stream);
-
-// Dynamic LDS bytes of a decode workgroup.
-size_t decode_lds_bytes_for(int head_size, int group, int waves);
 
 }  // namespace pa

@@ -112,8 +112,8 @@ def gpu_step(w: Workload, partition_size: Optional[int] = None, out_dtype=torch.
         pa.pa_decode(out, w.query, kc, vc, bt, cl, w.scale)
     else:
         mcl = w.max_context_len if max_context_len is None else max_context_len
-        nbytes = pa.pa_decode_partitioned_workspace_size(S, Hq, D, mcl, partition_size)
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=kc.device)
+        ws = pa.decode_workspace(S, Hq, D, mcl, partition_size, device=kc.device)
+        ws.fill_(0xFF)                  # NaN bit patterns: the call must not depend on them
         pa.pa_decode_partitioned(out, w.query, kc, vc, bt, cl, w.scale, mcl, partition_size, ws)
     torch.cuda.synchronize()
     return GpuResult(out, kc, vc, ws)

@@ -121,7 +121,8 @@ def test_workspace_size_formula(lib):
     for S, Hq, D, L, Ps in [(64, 32, 128, 4096, 256), (8, 64, 128, 32768, 512), (4, 4, 64, 37, 32),
                             (3, 2, 64, 0, 16), (1, 1, 64, 16, 16)]:
         R = S * Hq * max(1, -(-L // Ps))
-        assert pa.pa_decode_partitioned_workspace_size(S, Hq, D, L, Ps) == 2 * a256(4 * R) + a256(4 * R * D)
+        assert pa.pa_decode_partitioned_workspace_size(S, Hq, D, L, Ps) == \
+            2 * a256(4 * R) + a256(4 * R * D)
     assert pa.pa_decode_partitioned_workspace_size(-1, 4, 64, 10, 16) == 0
     assert pa.pa_decode_partitioned_workspace_size(1, 4, 64, 10, 0) == 0
 
