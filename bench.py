@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 METRIC = "decode attention KV-read GB/s (% of HBM peak) and seq-steps/sec at 1 GPU"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_456_amd", "csrc", "pa_decode.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_456_amd", "csrc", f)
+               for f in ("pa_decode.hip", "pa_api.cpp", "pa_internal.h")]
 
 
 def log(msg: str) -> None:
@@ -42,7 +43,10 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel: str, partition_size: int):
@@ -72,6 +76,9 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device-to-device copy of MIB MiB three times (a "
+                         "kernel of known traffic that scales the HBM byte counters of a profile)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -91,6 +98,15 @@ def main() -> int:
         return 1
     pa.load()
     dev = torch.device("cuda:0")
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 copies of {n} bytes")
+        del src, dst
     spec = wl.SPECS[args.workload]
     psize = args.partition_size or spec.partition_size
 
@@ -184,8 +200,10 @@ def main() -> int:
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode attention call (partition kernel + log-sum-exp reduce)"
-                      if args.kernel == "partitioned" else "pa_decode kernel",
+            "kernel": "attention call: paged_decode_persistent_kernel + lse_reduce_kernel"
+                      if args.kernel == "partitioned" else "paged_decode_kernel",
+            "timing": "HIP events around each attention call on its launch stream, mean over "
+                      "the timed steps",
         },
         "cpu_baseline": None,
     }

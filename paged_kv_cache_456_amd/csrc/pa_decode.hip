@@ -7,12 +7,16 @@
 // pages" on "What vLLM Is and Why It Exists"). The attention is standard
 // scaled dot-product softmax attention (the pages print no formula).
 //
-// Work decomposition. One workgroup per (KV head, sequence, context
-// partition); the single-pass entry point is the case of one partition that
-// spans the whole context. Every query head of the group that shares the KV
-// head is handled by the same wave, so each K/V byte is read from HBM once
-// per step. The partition's blocks are dealt out in rounds: in each round,
-// wave w takes BPW consecutive blocks.
+// Work decomposition. A work item is one context partition of one KV head
+// of one sequence; the single-pass entry point is the case of one partition
+// that spans the whole table. Every query head of the group that shares the
+// KV head is handled by the same wave, so each K/V byte is read from HBM once
+// per step. The partitioned entry point runs a persistent schedule: only as
+// many workgroups as the GPU keeps resident, each taking every grid-th item
+// of the list of items that exist (built from context_lens in LDS); the
+// single pass, and batches too large for that list, use one workgroup per
+// item. An item's blocks are dealt out in rounds: in each round, wave w takes
+// BPW consecutive blocks.
 //
 // Per round, per wave:
 //   * physical block ids come from a per-wave register holding the wave's
