@@ -111,7 +111,17 @@ def main() -> int:
     psize = args.partition_size or spec.partition_size
 
     # Replicas of the batch: same lengths, independent placement and values.
-    base = wl.make_workload(args.workload, device=dev)
+    nb = None
+    if spec.pool.startswith("hbm"):
+        # A pool sized to a share of HBM: one replica (its KV is far beyond the
+        # Infinity Cache anyway), capped by the memory that is actually free.
+        args.replicas = 1
+        free, _ = torch.cuda.mem_get_info()
+        per_block = 2 * spec.num_kv_heads * wl.BLOCK_SIZE * spec.head_size * \
+            torch.tensor([], dtype=spec.dtype).element_size()
+        want = float(spec.pool.split(":")[1]) * wl.HBM_BYTES
+        nb = int(min(want, 0.85 * free) // per_block)
+    base = wl.make_workload(args.workload, device=dev, num_blocks=nb, poison=nb is None)
     lengths = base.context_lens.tolist()
     reps = [base] + [wl.make_workload(args.workload, device=dev, lengths=lengths, seed_offset=r)
                      for r in range(1, args.replicas)]
@@ -190,7 +200,8 @@ def main() -> int:
             "max_context_len": mcl, "kv_bytes_per_step": kv_bytes,
             "kernel": "pa_decode" if args.kernel == "single" else "pa_decode_partitioned",
             "partition_size": psize if args.kernel == "partitioned" else None,
-            "replicas": args.replicas, "step": "pa_reshape_and_cache + attention",
+            "replicas": args.replicas, "pool_blocks": base.num_blocks,
+            "step": "pa_reshape_and_cache + attention",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
