@@ -35,6 +35,7 @@ _ERRORS = {
     -4: "slot past the end of the pool",
     -5: "two tokens write the same slot",
     -6: "out of memory",
+    -7: "block copy past the pool, or whose result would depend on the copy order",
 }
 
 
@@ -69,6 +70,9 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
                                               ctypes.c_int64, ctypes.c_double, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int]
     lib.oracle_decode_partitioned.restype = ctypes.c_int
+    lib.oracle_copy_blocks.argtypes = [u8p, u8p, i64p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64]
+    lib.oracle_copy_blocks.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -140,6 +144,25 @@ def reshape_and_cache(key: np.ndarray, value: np.ndarray, key_cache: np.ndarray,
     rc = lib.oracle_reshape_and_cache(key.ctypes.data, value.ctypes.data, key_cache.ctypes.data,
                                       value_cache.ctypes.data, _ptr(slots, ctypes.c_int64),
                                       T, Hkv, D, block_size, NB, key.dtype.itemsize)
+    _check(rc)
+
+
+def copy_blocks(key_cache: np.ndarray, value_cache: np.ndarray, block_mapping,
+                lib: Optional[ctypes.CDLL] = None) -> None:
+    """Copy-on-write block copy, in place, byte for byte: for each pair (src, dst) of
+    block_mapping ([N, 2] int64), block dst of both pools becomes a copy of block src.
+    Pools are [NB, Hkv, B, D] numpy arrays (bf16 as uint16 views), C-contiguous."""
+    lib = lib or _lib()
+    for a in (key_cache, value_cache):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("arrays must be C-contiguous")
+    if key_cache.shape != value_cache.shape or key_cache.dtype != value_cache.dtype:
+        raise ValueError("pools must share a shape and dtype")
+    pairs = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2))
+    NB = key_cache.shape[0]
+    block_bytes = key_cache.nbytes // NB if NB else 1
+    rc = lib.oracle_copy_blocks(key_cache.ctypes.data, value_cache.ctypes.data,
+                                _ptr(pairs, ctypes.c_int64), pairs.shape[0], block_bytes, NB)
     _check(rc)
 
 

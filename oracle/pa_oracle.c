@@ -64,7 +64,8 @@ enum {
     ORACLE_BAD_LEN = -3,    /* a context length is negative or beyond the table  */
     ORACLE_BAD_SLOT = -4,   /* a slot lies past the end of the pool              */
     ORACLE_DUP_SLOT = -5,   /* two tokens write the same slot                    */
-    ORACLE_NOMEM = -6
+    ORACLE_NOMEM = -6,
+    ORACLE_BAD_PAIR = -7    /* a block copy whose order would matter, or past pool */
 };
 
 /* ------------------------------------------------------------------------ */
@@ -366,6 +367,49 @@ int oracle_decode_partitioned(double* out, double* part_max, double* part_sum,
         free(K); free(V); free(l); free(mp); free(sp); free(op);
     }
     return failed ? ORACLE_NOMEM : ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block copy (copy-on-write)                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Copy-on-write ("Idea 1: PagedAttention", day-9 post, "Why this wins": when a
+ * shared block has to diverge, only the changed block is copied, not the
+ * whole cache). Each pair (src, dst) of block_mapping copies physical block
+ * src of both pools -- every KV head, every row, block_bytes bytes per pool --
+ * onto block dst, byte for byte. A pair with a negative id is skipped. A
+ * destination must not repeat and must not be any pair's source, so that the
+ * result cannot depend on the order of the copies; ids past the pool are
+ * errors too. Nothing is written when a check fails.
+ */
+int oracle_copy_blocks(uint8_t* key_cache, uint8_t* value_cache, const int64_t* block_mapping,
+                       int64_t num_pairs, int64_t block_bytes, int64_t num_blocks)
+{
+    if (num_pairs < 0 || block_bytes <= 0 || num_blocks < 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        if (src < 0 || dst < 0)
+            continue;
+        if (src >= num_blocks || dst >= num_blocks)
+            return ORACLE_BAD_PAIR;
+        for (int64_t j = 0; j < num_pairs; ++j) {
+            const int64_t s2 = block_mapping[2 * j], d2 = block_mapping[2 * j + 1];
+            if (s2 < 0 || d2 < 0)
+                continue;
+            if (dst == s2 || (j != i && dst == d2))
+                return ORACLE_BAD_PAIR;
+        }
+    }
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        if (src < 0 || dst < 0)
+            continue;
+        memcpy(key_cache + dst * block_bytes, key_cache + src * block_bytes, (size_t)block_bytes);
+        memcpy(value_cache + dst * block_bytes, value_cache + src * block_bytes, (size_t)block_bytes);
+    }
+    return ORACLE_OK;
 }
 
 int oracle_max_threads(void)

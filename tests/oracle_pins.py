@@ -389,4 +389,46 @@ def pin_scatter_rejects(lib):
         raise AssertionError(f"slots {slots} accepted")
 
 
+def pin_copy_blocks_positions(lib):
+    """Copy-on-write: block dst of both pools becomes block src, bit for bit, for every
+    head and row; pairs with a negative id are skipped; nothing else changes (day-9 post,
+    "Why this wins": only the changed block is copied)."""
+    rng = np.random.default_rng(30)
+    NB, Hkv, D = 9, 3, 8
+    kc = rng.integers(0, 1 << 16, size=(NB, Hkv, B, D), dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, size=(NB, Hkv, B, D), dtype=np.uint16)
+    kc[2, 1, 3, 0] = 0x7FC1
+    pairs = np.array([[2, 5], [-1, 0], [7, 1], [2, 8], [4, -1]], np.int64)
+    ek, ev = kc.copy(), vc.copy()
+    for src, dst in pairs:
+        if src >= 0 and dst >= 0:
+            ek[dst] = kc[src]
+            ev[dst] = vc[src]
+    oracle.copy_blocks(kc, vc, pairs, lib=lib)
+    assert np.array_equal(kc, ek) and np.array_equal(vc, ev)
+    assert np.array_equal(kc[5], kc[2]) and not np.array_equal(kc[5], vc[5])
+    f = rng.standard_normal((3, 1, B, 4)).astype(np.float32)
+    g = rng.standard_normal((3, 1, B, 4)).astype(np.float32)
+    f0, g0 = f.copy(), g.copy()
+    oracle.copy_blocks(f, g, [[0, 2]], lib=lib)
+    assert np.array_equal(f[2], f0[0]) and np.array_equal(g[2], g0[0])
+    assert np.array_equal(f[:2], f0[:2]) and np.array_equal(g[:2], g0[:2])
+
+
+def pin_copy_blocks_rejects(lib):
+    """Copies whose result would depend on their order (a repeated destination, a
+    destination that is a source) and ids past the pool are errors; nothing is written."""
+    rng = np.random.default_rng(31)
+    kc = rng.integers(0, 1 << 16, size=(4, 1, B, 4), dtype=np.uint16)
+    vc = kc.copy()
+    for pairs in ([[0, 1], [2, 1]], [[0, 1], [1, 2]], [[3, 3]], [[0, 4]], [[4, 0]]):
+        k0 = kc.copy()
+        try:
+            oracle.copy_blocks(kc, vc, pairs, lib=lib)
+        except oracle.OracleError:
+            assert np.array_equal(kc, k0)
+            continue
+        raise AssertionError(f"pairs {pairs} accepted")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -12,6 +12,10 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "pa_oracle.c")
 
 # (name, text in pa_oracle.c, replacement, occurrences expected)
 MUTANTS = [
+    ("copy_direction", "memcpy(key_cache + dst * block_bytes, key_cache + src * block_bytes,",
+     "memcpy(key_cache + src * block_bytes, key_cache + dst * block_bytes,", 1),
+    ("copy_v_from_k", "memcpy(value_cache + dst * block_bytes, value_cache + src * block_bytes,",
+     "memcpy(value_cache + dst * block_bytes, key_cache + src * block_bytes,", 1),
     ("gqa_interleaved", "const int h = kv * group + g;", "const int h = g * num_kv_heads + kv;", 2),
     ("scale_dropped", "l[t] = scale * dot;", "l[t] = dot;", 1),
     ("exp_sign", "l[t] = exp(l[t] - m);", "l[t] = exp(m - l[t]);", 1),
