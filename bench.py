@@ -70,6 +70,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
+                    help="decode: the decode step (default); copy_blocks: pa_copy_blocks alone")
     ap.add_argument("--workload", default="llama8b_gqa_bf16")
     ap.add_argument("--kernel", choices=("partitioned", "single"), default="partitioned")
     ap.add_argument("--partition-size", type=int, default=0, help="0 = the workload's default")
@@ -98,6 +100,8 @@ def main() -> int:
         return 1
     pa.load()
     dev = torch.device("cuda:0")
+    if args.op == "copy_blocks":
+        return bench_copy_blocks(args, dev)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -222,6 +226,61 @@ def main() -> int:
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(base, kv_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_copy_blocks(args, dev) -> int:
+    """pa_copy_blocks on the Llama-8B pool shapes (8 KV heads, D = 128, bf16: 32 KB per block
+    per pool): 2048 pairs per call (128 MB read + 128 MB written), four rotating mappings
+    over a 16384-block pool; and the copy-on-write of one block per sequence of the
+    prefix-shared batch (128 pairs), which is launch-bound. Synthetic data."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_456_amd as pa
+
+    Hkv, D, NB, npairs = 8, 128, 16384, 2048
+    block_bytes = Hkv * 16 * D * 2
+    kc = torch.empty((NB, Hkv, 16, D), dtype=torch.bfloat16, device=dev).normal_()
+    vc = torch.empty_like(kc).normal_()
+    rng = np.random.default_rng(5)
+    maps = []
+    for _ in range(4):
+        perm = rng.permutation(NB)
+        maps.append(torch.from_numpy(np.stack([perm[:npairs], perm[npairs:2 * npairs]], 1)).to(dev))
+    small = torch.from_numpy(np.stack([np.arange(128), 8192 + np.arange(128)], 1)).to(dev)
+
+    def timed(mapping_of, steps):
+        for i in range(args.warmup):
+            pa.pa_copy_blocks(kc, vc, mapping_of(i))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            pa.pa_copy_blocks(kc, vc, mapping_of(i))
+        e1.record()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps, e0.elapsed_time(e1) * 1e-3 / steps
+
+    wall, dev_s = timed(lambda i: maps[i % 4], args.steps)
+    _, small_s = timed(lambda i: small, args.steps)
+    moved = 2 * 2 * npairs * block_bytes            # both pools, read + write
+    gbs = moved / dev_s / 1e9
+    print(json.dumps({
+        "metric": "copy-on-write block copy GB/s (bytes read + written)", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "copy_blocks", "num_pairs": npairs, "num_kv_heads": Hkv,
+                   "head_size": D, "block_bytes_per_pool": block_bytes, "pool_blocks": NB},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "copy_blocks_kernel",
+                     "timing": "HIP events around the timed calls, mean per call"},
+        "cow_128_pairs_us": round(small_s * 1e6, 3),
+        "cpu_baseline": None,
+    }), flush=True)
     return 0
 
 

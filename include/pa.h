@@ -9,6 +9,7 @@
  * the two GPU operations of one decode step over such a cache:
  *
  *   pa_reshape_and_cache   write each new token's key and value into its slot
+ *   pa_copy_blocks         copy whole blocks (copy-on-write of a shared block)
  *   pa_decode              one query token per sequence attends over its
  *                          block-scattered context (single pass)
  *   pa_decode_partitioned  the same result, with each context cut into
@@ -105,6 +106,26 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value,
                                  const int64_t* slot_mapping, int64_t num_tokens,
                                  int num_kv_heads, int head_size, int block_size,
                                  int64_t num_blocks, pa_dtype_t kv_dtype, void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole blocks within the pools (copy-on-write).
+ *
+ * When a block shared by several sequences must diverge, only that block is
+ * copied ("Idea 1: PagedAttention" on the day-9 post, "Why this wins"). For
+ * each pair i, block block_mapping[2i] of both pools (every KV head, every
+ * row) is copied onto block block_mapping[2i + 1], byte for byte.
+ *
+ *   block_mapping  int64 [num_pairs][2] (source, destination), device memory.
+ *                  A pair with a negative id, or an id >= num_blocks, is
+ *                  skipped. Destinations must be distinct and must not be the
+ *                  source of any pair: the copies run in parallel, in no order.
+ *   key_cache, value_cache  [NB][Hkv][16][D] of kv_dtype, updated in place.
+ *
+ * num_pairs = 0 is valid and enqueues nothing.
+ */
+pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                           int64_t num_pairs, int num_kv_heads, int head_size, int block_size,
+                           int64_t num_blocks, pa_dtype_t kv_dtype, void* stream);
 
 /*
  * pa_decode -- single-pass paged decode attention.

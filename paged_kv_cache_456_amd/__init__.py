@@ -4,11 +4,12 @@ The GPU work lives in ``libpa.so`` (hand-written HIP kernels behind the C-ABI
 declared in ``include/pa.h``). This package is its thin Python binding:
 
     pa_reshape_and_cache   write new tokens' K/V into their cache slots
+    pa_copy_blocks         copy whole blocks (copy-on-write)
     pa_decode              single-pass paged decode attention
     pa_decode_partitioned  split-context decode with a log-sum-exp reduce
 """
 from ._lib import (  # noqa: F401
-    PA_BF16, PA_F32, PagedAttentionError, decode_workspace, load, pa_decode,
+    PA_BF16, PA_F32, PagedAttentionError, decode_workspace, load, pa_copy_blocks, pa_decode,
     pa_decode_partitioned, pa_decode_partitioned_workspace_size, pa_reshape_and_cache,
     pa_status_str, workspace_partials,
 )

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_F32, PA_BF16 = 0, 1
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, 1, 2, 3, 4
 
-EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_partitioned",
+EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_partitioned",
            "pa_decode_partitioned_workspace_size", "pa_status_str")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -42,6 +42,8 @@ def load() -> ctypes.CDLL:
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
     lib.pa_reshape_and_cache.restype = i32
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
+    lib.pa_copy_blocks.restype = i32
     lib.pa_decode.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i64,
                               f32, vp]
     lib.pa_decode.restype = i32
@@ -111,6 +113,22 @@ def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torc
                                      value_cache.data_ptr(), slot_mapping.data_ptr(), T, Hkv, D, B,
                                      NB, _dtype_code(key.dtype), _stream(key, stream))
     _check(rc, "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                   block_mapping: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Copy block block_mapping[i, 0] of both pools onto block block_mapping[i, 1]
+    (int64 [N, 2] on the GPU), asynchronously on the stream."""
+    _dev(key_cache, value_cache, block_mapping)
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise TypeError("block_mapping must be int64 [N, 2]")
+    NB, Hkv, B, D = key_cache.shape
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key and value pools must share a shape and dtype")
+    rc = load().pa_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), block_mapping.data_ptr(),
+                               block_mapping.shape[0], Hkv, D, B, NB, _dtype_code(key_cache.dtype),
+                               _stream(key_cache, stream))
+    _check(rc, "pa_copy_blocks")
 
 
 def _decode_common(out, query, key_cache, value_cache, block_tables, context_lens):

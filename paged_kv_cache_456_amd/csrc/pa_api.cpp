@@ -148,6 +148,34 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* key_c
     return from_hip(pa::launch_cache(p, num_tokens, static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                           int64_t num_pairs, int num_kv_heads, int head_size, int block_size,
+                           int64_t num_blocks, pa_dtype_t kv_dtype, void* stream) {
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks < 0)
+        return PA_EINVAL;
+    if (!dtype_ok(kv_dtype) || block_size != pa::kBlockSize || (head_size != 64 && head_size != 128))
+        return PA_EUNSUPPORTED;
+    if (num_pairs > INT32_MAX)
+        return PA_EUNSUPPORTED;
+    if (num_pairs == 0)
+        return PA_OK;
+    if (!key_cache || !value_cache || !block_mapping)
+        return PA_EINVAL;
+    if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(block_mapping, 8))
+        return PA_EINVAL;
+    const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * pa::kBlockSize * head_size *
+                                elem_bytes(kv_dtype);
+    if (num_blocks > INT64_MAX / block_bytes)
+        return PA_EINVAL;
+    pa::CopyParams p{};
+    p.key_cache = static_cast<uint8_t*>(key_cache);
+    p.value_cache = static_cast<uint8_t*>(value_cache);
+    p.block_mapping = block_mapping;
+    p.num_blocks = num_blocks;
+    p.block_bytes = block_bytes;
+    return from_hip(pa::launch_copy_blocks(p, num_pairs, static_cast<hipStream_t>(stream)));
+}
+
 pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* query, const void* key_cache,
                       const void* value_cache, pa_dtype_t kv_dtype, const int32_t* block_tables,
                       int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,

@@ -42,7 +42,49 @@ __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(CacheP
     }
 }
 
+// Copy-on-write block copy ("Idea 1: PagedAttention" on the day-9 post: when
+// a shared block must diverge, only that block is copied). Each pair
+// (src, dst) copies physical block src of both pools onto block dst. Grid:
+// (pairs, 2 pools); a workgroup streams one block of one pool
+// (Hkv * 16 * D * elem bytes) in 16-byte pieces, kCopyUnroll pieces in flight
+// per thread, past the caches (nothing reads the copy in this kernel).
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 8;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyParams p) {
+    const int64_t i = blockIdx.x;
+    const int64_t src = p.block_mapping[2 * i];
+    const int64_t dst = p.block_mapping[2 * i + 1];
+    if (src < 0 || dst < 0 || src >= p.num_blocks || dst >= p.num_blocks)
+        return;                                    // skipped pair, or an id outside the pool
+    uint8_t* pool = blockIdx.y ? p.value_cache : p.key_cache;
+    const u32x4* from = reinterpret_cast<const u32x4*>(pool + src * p.block_bytes);
+    u32x4* to = reinterpret_cast<u32x4*>(pool + dst * p.block_bytes);
+    const int64_t n = p.block_bytes / 16;
+    for (int64_t c0 = threadIdx.x; c0 < n; c0 += static_cast<int64_t>(blockDim.x) * kCopyUnroll) {
+        u32x4 v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int64_t c = c0 + static_cast<int64_t>(u) * blockDim.x;
+            if (c < n)
+                v[u] = __builtin_nontemporal_load(from + c);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int64_t c = c0 + static_cast<int64_t>(u) * blockDim.x;
+            if (c < n)
+                __builtin_nontemporal_store(v[u], to + c);
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyParams& p, int64_t num_pairs, hipStream_t stream) {
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(num_pairs), 2),
+                       dim3(kCopyThreads), 0, stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_cache(const CacheParams& p, int64_t num_tokens, hipStream_t stream) {
     const int pieces = 2 * p.num_kv_heads * (p.row_bytes / 16);

@@ -114,11 +114,20 @@ constexpr size_t persistent_lds_bytes(int num_seqs) {
     return sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1 + 2 * kItemListCap);
 }
 
+struct CopyParams {
+    uint8_t* key_cache;
+    uint8_t* value_cache;
+    const int64_t* block_mapping;  // [N][2]: source block, destination block
+    int64_t num_blocks;
+    int64_t block_bytes;           // Hkv * 16 * D * element bytes
+};
+
 // Launchers (pa_decode.hip, pa_cache.hip). kv: 0 = fp32, 1 = bf16.
 hipError_t launch_decode(const DecodeParams& p, int kv_bf16, int head_size, int out_bf16,
                          int num_seqs, int grid_partitions, int waves, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, int head_size, int out_bf16, int num_seqs,
                          hipStream_t stream);
 hipError_t launch_cache(const CacheParams& p, int64_t num_tokens, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyParams& p, int64_t num_pairs, hipStream_t stream);
 
 }  // namespace pa

@@ -64,6 +64,24 @@ def test_cache_checks(lib, kw, expect):
     assert cache_call(lib, **kw) == expect
 
 
+def copy_call(lib, **kw):
+    a = dict(kc=P, vc=P, map=P, N=3, Hkv=4, D=64, B=16, NB=32, dt=1)
+    a.update(kw)
+    return lib.pa_copy_blocks(a["kc"], a["vc"], a["map"], a["N"], a["Hkv"], a["D"], a["B"], a["NB"],
+                              a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=0), OK), (dict(N=0, map=0), OK),
+    (dict(N=-1), EINVAL), (dict(Hkv=0), EINVAL), (dict(NB=-1), EINVAL), (dict(D=0), EINVAL),
+    (dict(B=32), EUNSUP), (dict(D=80), EUNSUP), (dict(dt=7), EUNSUP), (dict(N=1 << 32), EUNSUP),
+    (dict(kc=0), EINVAL), (dict(map=0), EINVAL), (dict(vc=P + 8), EINVAL), (dict(map=P + 4), EINVAL),
+    (dict(NB=1 << 62), EINVAL),
+])
+def test_copy_checks(lib, kw, expect):
+    assert copy_call(lib, **kw) == expect
+
+
 def decode_args(**kw):
     a = dict(out=P, out_dt=0, q=P, kc=P, vc=P, kv_dt=0, bt=P, MB=3, cl=P, S=4, Hq=4, Hkv=4, D=64,
              B=16, NB=32, scale=0.125)

@@ -318,6 +318,54 @@ def test_scatter_skips_padding_and_out_of_pool_slots():
     assert torch.equal(_bits16(vc), _bits16(w.value_cache))
 
 
+def test_copy_blocks_bit_exact():
+    """pa_copy_blocks against the oracle's block copy, bit for bit on the whole pool (NaN
+    payloads included), with skipped and out-of-pool pairs, in bf16 and fp32."""
+    gen = torch.Generator().manual_seed(41)
+    for dtype, Hkv, D in ((torch.bfloat16, 8, 128), (torch.float32, 3, 64), (torch.bfloat16, 2, 64)):
+        NB = 300
+        ib = torch.int16 if dtype == torch.bfloat16 else torch.int32
+        kc = torch.randint(-30000, 30000, (NB, Hkv, 16, D), generator=gen, dtype=torch.int32).to(ib)
+        vc = torch.randint(-30000, 30000, (NB, Hkv, 16, D), generator=gen, dtype=torch.int32).to(ib)
+        perm = torch.randperm(NB, generator=gen)
+        pairs = torch.stack([perm[:100], perm[100:200]], 1).long()
+        pairs[3, 0] = -1
+        pairs[7, 1] = -5
+        pairs[11, 1] = NB + 2                   # outside the pool: skipped by the kernel
+        kref, vref = kc.numpy().copy(), vc.numpy().copy()
+        valid = pairs[(pairs >= 0).all(1) & (pairs < NB).all(1)]
+        oracle.copy_blocks(kref, vref, valid.numpy())
+        gk, gv = kc.view(dtype).cuda(), vc.view(dtype).cuda()
+        pa.pa_copy_blocks(gk, gv, pairs.cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(gk.cpu().view(ib), torch.from_numpy(kref))
+        assert torch.equal(gv.cpu().view(ib), torch.from_numpy(vref))
+
+
+def test_copy_on_write_then_decode():
+    """Copy-on-write of a shared prefix block for one sequence: after pa_copy_blocks and the
+    table update, decode output is bit-identical (the copy holds the same bytes), and a write
+    into the copy changes only that sequence's output."""
+    w = wl.make_workload("prefix_shared_bf16", device="cuda")
+    base = gpu_step(w, partition_size=512)
+    spare = int(np.setdiff1d(np.arange(w.num_blocks), w.used_blocks)[5])
+    shared = int(w.shared_blocks[10])
+    pa.pa_copy_blocks(base.key_cache, base.value_cache,
+                      torch.tensor([[shared, spare]], dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    bt = w.block_tables.copy()
+    bt[3, 10] = spare
+    w2 = wl.Workload(**{**w.__dict__, "key_cache": base.key_cache, "value_cache": base.value_cache,
+                        "block_tables": bt})
+    again = gpu_step(w2, partition_size=512, scatter=False)
+    assert torch.equal(again.out, base.out)
+    base.value_cache[spare].add_(1.0)
+    torch.cuda.synchronize()
+    changed = gpu_step(w2, partition_size=512, scatter=False)
+    diff = (changed.out - base.out).abs().amax(dim=(1, 2))
+    assert diff[3] > 0 and torch.count_nonzero(diff).item() == 1
+
+
 def test_empty_batch_and_side_stream():
     w = wl.make_workload("tiny_fp32", device="cuda")
     r = oracle_step(w)
