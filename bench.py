@@ -3,7 +3,8 @@
 
 One step = the cache write of each sequence's new token (pa_reshape_and_cache)
 followed by paged decode attention over every sequence's context
-(pa_decode_partitioned by default, pa_decode with --kernel single). The
+(pa_decode_partitioned by default, pa_decode with --kernel single,
+pa_decode_cascade with --kernel cascade on a shared-prefix workload). The
 default workload is the Llama-8B-shaped GQA batch: 64 sequences, 32 query /
 8 KV heads, head size 128, bf16 KV, context lengths min(4096, 100 +
 floor(Exp(mean 400))), 16-token blocks scattered through a pool twice the size
@@ -73,7 +74,9 @@ def main() -> int:
     ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
                     help="decode: the decode step (default); copy_blocks: pa_copy_blocks alone")
     ap.add_argument("--workload", default="llama8b_gqa_bf16")
-    ap.add_argument("--kernel", choices=("partitioned", "single"), default="partitioned")
+    ap.add_argument("--kernel", choices=("partitioned", "single", "cascade"), default="partitioned",
+                    help="cascade: pa_decode_cascade over the prefix every table shares "
+                         "(shared-prefix workloads only)")
     ap.add_argument("--partition-size", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -133,13 +136,27 @@ def main() -> int:
     Hkv = spec.num_kv_heads
     kv_bytes = base.kv_bytes()
     mcl = base.max_context_len
+    npb = 0
+    unique_bytes = kv_bytes
+    if args.kernel == "cascade":
+        if base.shared_blocks is None:
+            print(f"--kernel cascade needs a shared-prefix workload, not {args.workload}",
+                  file=sys.stderr)
+            return 2
+        # Every table starts with the same npb blocks: the prefix is read once per
+        # step, each suffix once.
+        npb = len(base.shared_blocks)
+        prefix_tokens = npb * wl.BLOCK_SIZE
+        tok = prefix_tokens + int((base.context_lens.astype(np.int64) - prefix_tokens).sum())
+        unique_bytes = tok * Hkv * D * torch.tensor([], dtype=spec.dtype).element_size() * 2
     inputs = []
     for w in reps:
         inputs.append(dict(
             w=w, bt=torch.from_numpy(w.block_tables).to(dev), cl=torch.from_numpy(w.context_lens).to(dev),
             slots=torch.from_numpy(w.slot_mapping).to(dev),
             out=torch.empty((S, Hq, D), dtype=torch.float32, device=dev),
-            ws=pa.decode_workspace(S, Hq, D, mcl, psize, device=dev)))
+            ws=pa.cascade_workspace(S, Hq, D, mcl, psize, npb, device=dev) if npb
+            else pa.decode_workspace(S, Hq, D, mcl, psize, device=dev)))
     torch.cuda.synchronize()
     log(f"[bench] {args.workload}: S={S} Hq={Hq} Hkv={Hkv} D={D} sum(L)={int(base.context_lens.sum())} "
         f"KV bytes/step={kv_bytes / 1e6:.1f} MB, replicas={args.replicas}, kernel={args.kernel}, P={psize}")
@@ -148,6 +165,9 @@ def main() -> int:
         w = x["w"]
         if args.kernel == "single":
             pa.pa_decode(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"], w.scale)
+        elif args.kernel == "cascade":
+            pa.pa_decode_cascade(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"],
+                                 w.scale, npb, mcl, psize, x["ws"])
         else:
             pa.pa_decode_partitioned(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"],
                                      w.scale, mcl, psize, x["ws"])
@@ -182,7 +202,9 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / args.steps
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     attn_ms = float(np.mean(call_ms))
-    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    # Algorithmic bytes of the attention call: the KV it must read (for the
+    # cascade, the shared prefix once and every suffix once).
+    achieved = unique_bytes / (attn_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload, args.kernel, psize)
 
     result = {
@@ -202,8 +224,11 @@ def main() -> int:
             "workload": args.workload, "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_size": D, "block_size": 16, "sum_context_len": int(base.context_lens.sum()),
             "max_context_len": mcl, "kv_bytes_per_step": kv_bytes,
-            "kernel": "pa_decode" if args.kernel == "single" else "pa_decode_partitioned",
-            "partition_size": psize if args.kernel == "partitioned" else None,
+            "kernel": {"single": "pa_decode", "partitioned": "pa_decode_partitioned",
+                       "cascade": "pa_decode_cascade"}[args.kernel],
+            "partition_size": psize if args.kernel != "single" else None,
+            "unique_kv_bytes_per_step": unique_bytes,
+            "prefix_blocks": npb or None,
             "replicas": args.replicas, "pool_blocks": base.num_blocks,
             "step": "pa_reshape_and_cache + attention",
         },
@@ -215,8 +240,11 @@ def main() -> int:
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "attention call: paged_decode_persistent_kernel + lse_reduce_kernel"
-                      if args.kernel == "partitioned" else "paged_decode_kernel",
+            "kernel": {"single": "paged_decode_kernel",
+                       "partitioned": "attention call: paged_decode_persistent_kernel + "
+                                      "lse_reduce_kernel",
+                       "cascade": "attention call: cascade_prefix_kernel + "
+                                  "paged_decode_persistent_kernel + lse_reduce_kernel"}[args.kernel],
             "timing": "HIP events around each attention call on its launch stream, mean over "
                       "the timed steps",
         },

@@ -15,6 +15,10 @@
  *   pa_decode_partitioned  the same result, with each context cut into
  *                          fixed-size partitions that run in parallel and a
  *                          log-sum-exp reduce across partitions
+ *   pa_decode_cascade      the same result for a batch whose tables all begin
+ *                          with the same physical blocks (a shared prefix):
+ *                          the prefix is read once per KV head for the whole
+ *                          batch instead of once per sequence
  *
  * Conventions shared by every call
  * --------------------------------
@@ -198,6 +202,72 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
                                   int head_size, int block_size, int64_t num_blocks,
                                   float scale, int max_context_len, int partition_size,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes pa_decode_cascade needs. With
+ *   NPs = max(1, ceil(max(max_context_len - 16 * num_prefix_blocks, 0) / partition_size))
+ *   NC  = ceil(num_prefix_blocks / 32),  NP = NPs + NC,  R = S * Hq * NP,
+ * the layout and size formula are those of the partitioned workspace:
+ *     2 * round_up(4 R, 256) + round_up(4 R D, 256).
+ * Returns 0 when an argument is out of range.
+ */
+size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_size,
+                                        int max_context_len, int partition_size,
+                                        int num_prefix_blocks);
+
+/*
+ * pa_decode_cascade -- decode attention over a shared prefix plus per-sequence
+ * suffixes.
+ *
+ * Two requests with a common prefix can map the same physical blocks ("Idea
+ * 1: PagedAttention" on the day-9 post, "Why this wins"). When the first
+ * num_prefix_blocks entries of EVERY block table are the same block ids, the
+ * prefix keys and values are the same for every sequence, so the prefix part
+ * of the attention is one dense product per KV head over all S * G query rows
+ * (G = Hq / Hkv). This call computes:
+ *   1. the prefix, in chunks of 32 blocks, for all query rows at once (K and V
+ *      read once per KV head, not once per sequence);
+ *   2. each sequence's suffix, tokens [16 * num_prefix_blocks, L), through
+ *      block-table entries num_prefix_blocks .. MB - 1, in partitions of
+ *      partition_size tokens (as pa_decode_partitioned);
+ *   3. the log-sum-exp combination of the prefix chunks and suffix partitions
+ *      (the same formula as pa_decode_partitioned).
+ * The result equals pa_decode on the same inputs, up to fp32 rounding order:
+ * the same softmax attention of each query over all L tokens of its context.
+ * (The pages name the sharing but give no kernel for it; this split is the
+ * standard log-sum-exp decomposition of softmax over disjoint token sets.)
+ *
+ *   kv_dtype           PA_BF16 only (PA_EUNSUPPORTED otherwise); out_dtype
+ *                      PA_F32 or PA_BF16.
+ *   num_prefix_blocks  1 <= num_prefix_blocks <= MB. The prefix ids are read
+ *                      from row 0 of block_tables; the caller guarantees that
+ *                      every other row starts with the same ids (the call
+ *                      does not compare them). Every context must hold the
+ *                      whole prefix: L < 16 * num_prefix_blocks gives a NaN
+ *                      row, as does a prefix id outside [0, NB) (for every
+ *                      sequence) or a suffix id outside [0, NB).
+ *   max_context_len    an upper bound on every context_lens[s]; it sizes the
+ *                      suffix partitions. A longer context gives NaN.
+ *   partition_size     suffix tokens per partition, a positive multiple of 16.
+ *   num_blocks         NB >= 1 (PA_EINVAL for an empty pool).
+ *   workspace          device scratch of at least
+ *                      pa_decode_cascade_workspace_size(...) bytes, 256-byte
+ *                      aligned, float32 part_max [S][Hq][NP], part_sum
+ *                      [S][Hq][NP], part_out [S][Hq][NP][D]: slots
+ *                      0 .. NPs - 1 of a row hold suffix partitions, slots
+ *                      NPs .. NP - 1 the prefix chunks. Its contents before
+ *                      the call do not matter; after it they are unspecified.
+ *   num_seqs = 0 is valid and enqueues nothing. Other arguments and errors
+ *   are those of pa_decode_partitioned.
+ */
+pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query,
+                              const void* key_cache, const void* value_cache, pa_dtype_t kv_dtype,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int num_seqs, int num_q_heads,
+                              int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                              float scale, int num_prefix_blocks, int max_context_len,
+                              int partition_size, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* A static, human-readable name for a status code. */
 const char* pa_status_str(pa_status_t status);

@@ -18,7 +18,8 @@ PA_F32, PA_BF16 = 0, 1
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, 1, 2, 3, 4
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_partitioned",
-           "pa_decode_partitioned_workspace_size", "pa_status_str")
+           "pa_decode_partitioned_workspace_size", "pa_decode_cascade",
+           "pa_decode_cascade_workspace_size", "pa_status_str")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -52,6 +53,11 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_partitioned.restype = i32
     lib.pa_decode_partitioned_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.pa_decode_partitioned_workspace_size.restype = sz
+    lib.pa_decode_cascade.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32,
+                                      i32, i64, f32, i32, i32, i32, vp, sz, vp]
+    lib.pa_decode_cascade.restype = i32
+    lib.pa_decode_cascade_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_cascade_workspace_size.restype = sz
     lib.pa_status_str.argtypes = [i32]
     lib.pa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -186,6 +192,46 @@ def pa_decode_partitioned(out: torch.Tensor, query: torch.Tensor, key_cache: tor
                                       _stream(query, stream))
     _check(rc, "pa_decode_partitioned")
     return out
+
+
+def pa_decode_cascade_workspace_size(num_seqs: int, num_q_heads: int, head_size: int,
+                                     max_context_len: int, partition_size: int,
+                                     num_prefix_blocks: int) -> int:
+    return int(load().pa_decode_cascade_workspace_size(num_seqs, num_q_heads, head_size,
+                                                       max_context_len, partition_size,
+                                                       num_prefix_blocks))
+
+
+def pa_decode_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, scale: float, num_prefix_blocks: int,
+                      max_context_len: int, partition_size: int, workspace: torch.Tensor,
+                      stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Decode attention for a batch whose block tables all start with the same
+    num_prefix_blocks ids (read from row 0). workspace is a uint8 GPU tensor of at least
+    pa_decode_cascade_workspace_size(...) bytes (cascade_workspace() makes one)."""
+    S, Hq, Hkv, D, B, NB, MB = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                              context_lens)
+    _dev(workspace)
+    rc = load().pa_decode_cascade(out.data_ptr(), _dtype_code(out.dtype), query.data_ptr(),
+                                  key_cache.data_ptr(), value_cache.data_ptr(),
+                                  _dtype_code(key_cache.dtype), block_tables.data_ptr(), MB,
+                                  context_lens.data_ptr(), S, Hq, Hkv, D, B, NB, float(scale),
+                                  int(num_prefix_blocks), int(max_context_len), int(partition_size),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(query, stream))
+    _check(rc, "pa_decode_cascade")
+    return out
+
+
+def cascade_workspace(num_seqs: int, num_q_heads: int, head_size: int, max_context_len: int,
+                      partition_size: int, num_prefix_blocks: int, device=None) -> torch.Tensor:
+    """An uninitialised uint8 GPU workspace of the size pa_decode_cascade needs."""
+    n = pa_decode_cascade_workspace_size(num_seqs, num_q_heads, head_size, max_context_len,
+                                         partition_size, num_prefix_blocks)
+    if n == 0:
+        raise ValueError("workspace size out of range")
+    return torch.empty(n, dtype=torch.uint8, device=device if device is not None else "cuda")
 
 
 def decode_workspace(num_seqs: int, num_q_heads: int, head_size: int, max_context_len: int,

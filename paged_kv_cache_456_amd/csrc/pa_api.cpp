@@ -193,6 +193,8 @@ pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* query, const 
     p.out = out;
     p.partition_blocks = max_blocks_per_seq;
     p.num_partitions = 1;
+    p.part_stride = 1;
+    p.table_blocks = max_blocks_per_seq;
     p.num_seqs = num_seqs;
     p.persistent = 0;
     const int waves = choose_waves(max_blocks_per_seq, elem_bytes(kv_dtype), head_size, p.group,
@@ -257,6 +259,8 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
     p.part_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
     p.partition_blocks = partition_size / pa::kBlockSize;
     p.num_partitions = np;
+    p.part_stride = np;
+    p.table_blocks = max_blocks_per_seq;
     p.num_seqs = num_seqs;
     p.persistent = num_seqs <= pa::kMaxPersistentSeqs && num_kv_heads <= pa::kMaxPersistentKvHeads;
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -281,7 +285,147 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
     r.num_kv_heads = num_kv_heads;
     r.group = p.group;
     r.num_partitions = np;
+    r.part_stride = np;
     r.partition_blocks = p.partition_blocks;
+    r.table_blocks = max_blocks_per_seq;
+    return from_hip(pa::launch_reduce(r, head_size, out_dtype == PA_BF16, num_seqs, s));
+}
+
+// Partitions of a cascade call: the suffix partitions (tokens past the shared
+// prefix, at most max_context_len - 16 * num_prefix_blocks) and one slot per
+// prefix chunk.
+static void cascade_shape(int max_context_len, int partition_size, int num_prefix_blocks,
+                          int* suffix_parts, int* chunks) {
+    const int64_t suffix = static_cast<int64_t>(max_context_len) -
+                           static_cast<int64_t>(num_prefix_blocks) * pa::kBlockSize;
+    *suffix_parts = num_partitions(suffix > 0 ? static_cast<int>(suffix) : 0, partition_size);
+    *chunks = (num_prefix_blocks + pa::kCascadeChunkBlocks - 1) / pa::kCascadeChunkBlocks;
+}
+
+size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_size,
+                                        int max_context_len, int partition_size,
+                                        int num_prefix_blocks) {
+    if (num_seqs < 0 || num_q_heads <= 0 || head_size <= 0 || max_context_len < 0 ||
+        partition_size <= 0 || num_prefix_blocks <= 0)
+        return 0;
+    int sp = 0, ch = 0;
+    cascade_shape(max_context_len, partition_size, num_prefix_blocks, &sp, &ch);
+    const unsigned __int128 rows = static_cast<unsigned __int128>(num_seqs) *
+                                   static_cast<unsigned __int128>(num_q_heads) *
+                                   static_cast<unsigned __int128>(sp + ch);
+    const unsigned __int128 bytes = 2 * (rows * 4 + 256) + rows * 4 * head_size + 256;
+    if (bytes > static_cast<unsigned __int128>(SIZE_MAX / 2))
+        return 0;
+    const size_t r = static_cast<size_t>(rows);
+    return 2 * align256(r * sizeof(float)) + align256(r * sizeof(float) * head_size);
+}
+
+pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query,
+                              const void* key_cache, const void* value_cache, pa_dtype_t kv_dtype,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int num_seqs, int num_q_heads,
+                              int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                              float scale, int num_prefix_blocks, int max_context_len,
+                              int partition_size, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    pa_status_t st = check_decode(out, out_dtype, query, key_cache, value_cache, kv_dtype,
+                                  block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                  scale);
+    if (st != PA_OK)
+        return st;
+    if (kv_dtype != PA_BF16)
+        return PA_EUNSUPPORTED;
+    if (max_context_len < 0 || partition_size <= 0 || partition_size % pa::kBlockSize != 0 ||
+        num_prefix_blocks <= 0 || num_prefix_blocks > max_blocks_per_seq || num_blocks == 0)
+        return PA_EINVAL;
+    int sp = 0, ch = 0;
+    cascade_shape(max_context_len, partition_size, num_prefix_blocks, &sp, &ch);
+    if (sp + ch > kMaxGridYZ)
+        return PA_EUNSUPPORTED;
+    if (num_seqs == 0)
+        return PA_OK;
+    const size_t need = pa_decode_cascade_workspace_size(num_seqs, num_q_heads, head_size,
+                                                         max_context_len, partition_size,
+                                                         num_prefix_blocks);
+    if (need == 0)
+        return PA_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < need)
+        return PA_EWORKSPACE;
+    if (!aligned(workspace, 256))
+        return PA_EINVAL;
+
+    const int np = sp + ch;
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * np;
+    char* ws = static_cast<char*>(workspace);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    pa::DecodeParams p = make_params(query, key_cache, value_cache, block_tables,
+                                     max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads,
+                                     num_blocks, scale);
+    p.out = out;
+    p.part_max = reinterpret_cast<float*>(ws);
+    p.part_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+    p.part_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+    p.partition_blocks = partition_size / pa::kBlockSize;
+    p.num_partitions = sp;
+    p.part_stride = np;
+    p.num_seqs = num_seqs;
+    p.skip_blocks = num_prefix_blocks;
+    p.table_blocks = max_blocks_per_seq - num_prefix_blocks;
+    p.partials_only = 1;
+
+    // 1. The shared prefix: one dense pass per KV head for all query rows.
+    pa::CascadeParams c{};
+    c.q = query;
+    c.k_cache = key_cache;
+    c.v_cache = value_cache;
+    c.block_tables = block_tables;
+    c.part_max = p.part_max;
+    c.part_sum = p.part_sum;
+    c.part_out = p.part_out;
+    c.num_blocks = num_blocks;
+    c.num_prefix_blocks = num_prefix_blocks;
+    c.chunk_blocks = pa::kCascadeChunkBlocks;
+    c.num_seqs = num_seqs;
+    c.num_q_heads = num_q_heads;
+    c.num_kv_heads = num_kv_heads;
+    c.group = p.group;
+    c.part_stride = np;
+    c.slot_base = sp;
+    c.scale_log2 = p.scale_log2;
+    hipError_t e = pa::launch_cascade_prefix(c, head_size, ch, s);
+    if (e != hipSuccess)
+        return PA_EHIP;
+
+    // 2. Each sequence's own suffix, through its block table, as partials.
+    if (p.table_blocks > 0) {
+        p.persistent = num_seqs <= pa::kMaxPersistentSeqs && num_kv_heads <= pa::kMaxPersistentKvHeads;
+        const int waves = choose_waves(p.partition_blocks, elem_bytes(kv_dtype), head_size, p.group,
+                                       pa::kPartWaves);
+        e = pa::launch_decode(p, 1, head_size, out_dtype == PA_BF16, num_seqs, sp, waves, s);
+        if (e != hipSuccess)
+            return PA_EHIP;
+    }
+
+    // 3. Log-sum-exp combination of suffix partitions and prefix chunks.
+    pa::ReduceParams r{};
+    r.context_lens = context_lens;
+    r.part_max = p.part_max;
+    r.part_sum = p.part_sum;
+    r.part_out = p.part_out;
+    r.out = out;
+    r.num_blocks = num_blocks;
+    r.max_blocks_per_seq = max_blocks_per_seq;
+    r.num_q_heads = num_q_heads;
+    r.num_kv_heads = num_kv_heads;
+    r.group = p.group;
+    r.num_partitions = sp;
+    r.part_stride = np;
+    r.partition_blocks = p.partition_blocks;
+    r.skip_blocks = num_prefix_blocks;
+    r.table_blocks = p.table_blocks;
+    r.extra_base = sp;
+    r.extra_count = ch;
     return from_hip(pa::launch_reduce(r, head_size, out_dtype == PA_BF16, num_seqs, s));
 }
 

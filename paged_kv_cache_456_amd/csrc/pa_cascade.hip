@@ -1,0 +1,251 @@
+// pa_cascade.hip -- attention over a prefix that every sequence shares, for
+// gfx950 (CDNA4).
+//
+// Two requests with a common prefix can share the same physical blocks
+// ("Idea 1: PagedAttention" on the day-9 post, "Why this wins"). When every
+// sequence of a batch maps the same leading blocks, each KV head's prefix K
+// and V are the same for all S * G query rows that read that head, so the
+// prefix part of decode attention is a dense product: logits = Q K^T over
+// [S * G rows] x [prefix tokens], and P V. This kernel computes it once per
+// (KV head, 64-row tile, prefix chunk) on MFMA, and writes per-row partials
+// (max m, sum s, normalised output o) of the chunk into the partition slots
+// of the partitioned decode's workspace; the suffix of each sequence is
+// decoded by the paged kernel and the log-sum-exp reduce combines both, so
+// the result is the same attention as a plain decode over the whole context.
+//
+// Per workgroup (4 waves, 16 query rows each), per step of 32 prefix tokens
+// (two blocks):
+//   * K tiles are loaded straight into the MFMA B-operand layout (token =
+//     lane % 16), Q^T K on v_mfma_f32_16x16x32_bf16 gives logits[row][token];
+//   * online softmax per row (running max and sum, base 2); the row max is a
+//     16-lane DPP row reduction;
+//   * P goes through LDS into the A-operand layout and is split into a bf16
+//     high part and a bf16 remainder, so P.V keeps about 16 bits of P;
+//   * V is written to LDS transposed (token-contiguous rows, padded so that
+//     the B-operand reads are conflict-free) and P.V runs on MFMA with the
+//     output rows in the same lanes as the softmax state.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kStepTokens = 32;                 // two blocks per step
+constexpr int kVtStride = kStepTokens + 8;      // bf16 per transposed V row (80 bytes)
+constexpr int kPStride = kStepTokens + 4;       // floats per P row in LDS (144 bytes)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    x = fmaxf(x, dpp<0x140>(x));
+    return x;
+}
+
+__device__ __forceinline__ float row_sum16(float x) {
+    x = x + dpp<0xB1>(x);
+    x = x + dpp<0x4E>(x);
+    x = x + dpp<0x141>(x);
+    x = x + dpp<0x140>(x);
+    return x;
+}
+
+// fp32 -> bf16 bits, round to nearest even (P is finite and non-negative).
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_value(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(CascadeParams p) {
+    constexpr int ROW = D * 2;                  // bytes per token row (bf16)
+    constexpr int TILE = kBlockSize * ROW;
+    constexpr int CH = ROW / 16;                // 16-byte chunks per row
+    constexpr int NQ = CH / 4;                  // K chunks per lane per tile
+    constexpr int NT = D / 16;                  // 16-column output tiles
+
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D][kVtStride];
+    __shared__ __attribute__((aligned(16))) float pl[kCascadeWaves][16][kPStride];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+    const int kvh = blockIdx.x;
+    const int chunk = blockIdx.z;
+    const int G = p.group, Hq = p.num_q_heads, Hkv = p.num_kv_heads;
+    const int rows = p.num_seqs * G;
+    const int row0 = blockIdx.y * (kCascadeWaves * 16) + wave * 16;
+
+    // Query rows of this wave as the MFMA A operand: lane row r16.
+    u32x4 qa[NQ];
+    {
+        const int r = row0 + r16;
+        const bool live = r < rows;
+        const int seq = live ? r / G : 0, hh = live ? r - (r / G) * G : 0;
+        const char* qp = static_cast<const char*>(p.q) +
+                         ((int64_t)seq * Hq + (int64_t)kvh * G + hh) * ROW;
+#pragma unroll
+        for (int c = 0; c < NQ; ++c)
+            qa[c] = live ? *reinterpret_cast<const u32x4*>(qp + (g + 4 * c) * 16)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    typedef __attribute__((address_space(4))) const int32_t ctable_t;
+    ctable_t* ids = (ctable_t*)p.block_tables;   // row 0 holds the shared prefix
+    const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE;
+    const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE;
+    const int64_t blk_stride = (int64_t)Hkv * TILE;
+    const int cb0 = chunk * p.chunk_blocks;
+    const int cb1 = min(cb0 + p.chunk_blocks, p.num_prefix_blocks);
+
+    float m[4], lsum[4];
+    f32x4 o[NT];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        m[j] = -INFINITY;
+        lsum[j] = 0.0f;
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+        o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bool poisoned = false;
+
+    for (int jb = cb0; jb < cb1; jb += 2) {
+        const int nb = min(2, cb1 - jb);
+        int id[2];
+        id[0] = ids[jb];
+        id[1] = ids[jb + nb - 1];               // a lone last block is read twice, masked below
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            if (id[b] < 0 || static_cast<int64_t>(id[b]) >= p.num_blocks) {
+                poisoned = true;
+                id[b] = 0;
+            }
+        }
+        // K tiles in the B-operand layout: lane = token r16, chunks g + 4c.
+        u32x4 kt[2][NQ];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const char* kp = kbase + (int64_t)id[b] * blk_stride + r16 * ROW + g * 16;
+#pragma unroll
+            for (int c = 0; c < NQ; ++c)
+                kt[b][c] = *reinterpret_cast<const u32x4*>(kp + 64 * c);
+        }
+        // V of the step's 32 tokens, transposed into LDS by the whole workgroup.
+        for (int idx = threadIdx.x; idx < kStepTokens * CH; idx += blockDim.x) {
+            const int t = idx / CH, c = idx - (idx / CH) * CH;
+            const int vid = (t >> 4) ? id[1] : id[0];
+            const u32x4 v = *reinterpret_cast<const u32x4*>(
+                vbase + (int64_t)vid * blk_stride + (t & 15) * ROW + c * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vt[c * 8 + 2 * e][t] = static_cast<uint16_t>(v[e] & 0xFFFFu);
+                vt[c * 8 + 2 * e + 1][t] = static_cast<uint16_t>(v[e] >> 16);
+            }
+        }
+        // logits[row 4g+j][token b*16 + r16]
+        f32x4 acc[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int c = 0; c < NQ; ++c)
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
+                                                                 __builtin_bit_cast(bf16x8, kt[b][c]),
+                                                                 acc[b], 0, 0, 0);
+        }
+        float alpha[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float x0 = acc[0][j] * p.scale_log2;
+            const float x1 = nb > 1 ? acc[1][j] * p.scale_log2 : -INFINITY;
+            const float mn = fmaxf(m[j], row_max16(fmaxf(x0, x1)));
+            alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
+            const float p0 = __builtin_amdgcn_exp2f(x0 - mn);
+            const float p1 = __builtin_amdgcn_exp2f(x1 - mn);
+            lsum[j] = lsum[j] * alpha[j] + p0 + p1;
+            m[j] = mn;
+            pl[wave][4 * g + j][r16] = p0;
+            pl[wave][4 * g + j][16 + r16] = p1;
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[n][j] *= alpha[j];
+        __syncthreads();                        // P of every wave and all of V^T are in LDS
+        // P as the A operand (row r16, tokens 8g..8g+7), split into bf16 hi + lo.
+        u16x8 phi, plo;
+        {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(&pl[wave][r16][8 * g]);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(&pl[wave][r16][8 * g + 4]);
+            const float pv[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint16_t h = bf16_bits(pv[i]);
+                phi[i] = h;
+                plo[i] = bf16_bits(pv[i] - bf16_value(h));
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const u16x8 vb = *reinterpret_cast<const u16x8*>(&vt[n * 16 + r16][8 * g]);
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, phi),
+                                                           __builtin_bit_cast(bf16x8, vb), o[n], 0, 0, 0);
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo),
+                                                           __builtin_bit_cast(bf16x8, vb), o[n], 0, 0, 0);
+        }
+        __syncthreads();                        // LDS free for the next step
+    }
+
+    // Row partials of this chunk: rows 4g+j of the wave, columns n*16 + r16.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float srow = row_sum16(lsum[j]);
+        const int r = row0 + 4 * g + j;
+        if (r >= rows)
+            continue;
+        const int seq = r / G, hh = r - (r / G) * G;
+        const int64_t pi = ((int64_t)seq * Hq + (int64_t)kvh * G + hh) * p.part_stride +
+                           p.slot_base + chunk;
+        const float inv = 1.0f / srow;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            p.part_out[pi * D + n * 16 + r16] = poisoned ? __builtin_nanf("") : o[n][j] * inv;
+        if (r16 == 0) {
+            p.part_max[pi] = poisoned ? 0.0f : m[j] * kLn2;
+            p.part_sum[pi] = poisoned ? __builtin_nanf("") : srow;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_cascade_prefix(const CascadeParams& p, int head_size, int num_chunks,
+                                 hipStream_t stream) {
+    const int rows = p.num_seqs * p.group;
+    const dim3 grid(p.num_kv_heads, (rows + kCascadeWaves * 16 - 1) / (kCascadeWaves * 16), num_chunks);
+    if (head_size == 64)
+        hipLaunchKernelGGL(cascade_prefix_kernel<64>, grid, dim3(kCascadeWaves * kWave), 0, stream, p);
+    else
+        hipLaunchKernelGGL(cascade_prefix_kernel<128>, grid, dim3(kCascadeWaves * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace pa

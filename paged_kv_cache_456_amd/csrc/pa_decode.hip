@@ -186,6 +186,13 @@ __device__ __forceinline__ bool context_unreadable(int L, int max_blocks_per_seq
     return L < 0 || static_cast<int64_t>(L) > cap || (L > 0 && num_blocks <= 0);
 }
 
+// Tokens of a context that this call reads: those past the skipped leading
+// blocks; -1 (unreadable) when the context is shorter than what is skipped.
+__device__ __forceinline__ int call_len(int L, int skip_blocks) {
+    const int64_t skip = static_cast<int64_t>(skip_blocks) * kBlockSize;
+    return L < skip ? -1 : static_cast<int>(L - skip);
+}
+
 // One work item: the partition `part` of KV head `kvh` of sequence `s`
 // (context length L), computed by the whole workgroup. Writes the output row
 // directly when the context has a single partition, else the partition's
@@ -206,10 +213,10 @@ __device__ __forceinline__ void process_item(const DecodeParams& p, float* smem,
     const int nw = blockDim.x / kWave;
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads, G = p.group;
 
-    const bool bad_len = context_unreadable(L, p.max_blocks_per_seq, p.num_partitions,
+    const bool bad_len = context_unreadable(L, p.table_blocks, p.num_partitions,
                                             p.partition_blocks, p.num_blocks);
     if (bad_len || L == 0) {
-        if (part == 0) {
+        if (part == 0 && !p.partials_only) {
             const float fill = bad_len ? __builtin_nanf("") : 0.0f;
             for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
                 const int h = idx / D, d = idx - (idx / D) * D;
@@ -250,7 +257,7 @@ __device__ __forceinline__ void process_item(const DecodeParams& p, float* smem,
     const int64_t blk_stride = (int64_t)Hkv * TILE;
     const int koff = r16 * ROW + g * 16;            // + 64 c
     const int voff = vrow * ROW + vchunk * 16;      // + TPL * ROW * c
-    const int64_t tbl = (int64_t)s * p.max_blocks_per_seq;
+    const int64_t tbl = (int64_t)s * p.max_blocks_per_seq + p.skip_blocks;
 
     float m[4], lsum[4];
     float o[GMAX][EPC];
@@ -481,7 +488,7 @@ __device__ __forceinline__ void process_item(const DecodeParams& p, float* smem,
     __syncthreads();
 
     // Merge the waves in a fixed order.
-    const bool split = nparts > 1;
+    const bool split = nparts > 1 || p.partials_only;
     for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
         const int h = idx / D;
         const int d = idx - h * D;
@@ -498,7 +505,7 @@ __device__ __forceinline__ void process_item(const DecodeParams& p, float* smem,
         if (!split) {
             store_out<OUT>(p.out, row * D + d, acc / S);
         } else {
-            const int64_t pi = row * p.num_partitions + part;
+            const int64_t pi = row * p.part_stride + part;
             p.part_out[pi * D + d] = acc / S;
             if (d == 0) {
                 p.part_max[pi] = M * kLn2;
@@ -511,7 +518,7 @@ __device__ __forceinline__ void process_item(const DecodeParams& p, float* smem,
 // Work slots of a sequence in the persistent schedule: its partitions, or a
 // single slot (which writes the zero or NaN row) when there is nothing to read.
 __device__ __forceinline__ int sequence_slots(int L, const DecodeParams& p) {
-    if (L == 0 || context_unreadable(L, p.max_blocks_per_seq, p.num_partitions, p.partition_blocks,
+    if (L == 0 || context_unreadable(L, p.table_blocks, p.num_partitions, p.partition_blocks,
                                      p.num_blocks))
         return 1;
     const int nblk = (L + kBlockSize - 1) / kBlockSize;
@@ -528,7 +535,7 @@ template <typename KV, int D, int GMAX, typename OUT>
 __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeParams p) {
     extern __shared__ float smem[];
     process_item<KV, D, GMAX, OUT>(p, smem, blockIdx.x, blockIdx.y, blockIdx.z,
-                                   p.context_lens[blockIdx.y]);
+                                   call_len(p.context_lens[blockIdx.y], p.skip_blocks));
 }
 
 // Waves per SIMD the persistent kernel is register-allocated for: three
@@ -550,7 +557,7 @@ void paged_decode_persistent_kernel(DecodeParams p) {
     int* first_slot = lens + S;                 // [S + 1], exclusive prefix sum of slots
     int* list = first_slot + S + 1;             // [kItemListCap][2]: sequence, part << 8 | kvh
     for (int i = threadIdx.x; i < S; i += blockDim.x)
-        lens[i] = p.context_lens[i];
+        lens[i] = call_len(p.context_lens[i], p.skip_blocks);
     __syncthreads();
     if (threadIdx.x < kWave) {
         int carry = 0;
@@ -625,25 +632,37 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams
     const int wave = threadIdx.x / kWave;
     const int nw = blockDim.x / kWave;
     const int G = p.group, Hq = p.num_q_heads, NP = p.num_partitions;
-    const int L = p.context_lens[s];
-    if (L == 0 || context_unreadable(L, p.max_blocks_per_seq, NP, p.partition_blocks, p.num_blocks))
+    const int L = call_len(p.context_lens[s], p.skip_blocks);
+    const bool bad = context_unreadable(L, p.table_blocks, NP, p.partition_blocks, p.num_blocks);
+    if (p.extra_count == 0 && (bad || L == 0))
         return;                                // the partition kernel wrote this row
+    if (bad) {                                 // cascade: an unreadable suffix
+        for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+            const int h = idx / D, d = idx - (idx / D) * D;
+            store_out<OUT>(p.out, ((int64_t)s * Hq + kvh * G + h) * D + d, __builtin_nanf(""));
+        }
+        return;
+    }
     const int nblk = (L + kBlockSize - 1) / kBlockSize;
-    const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
-    if (nparts <= 1)
+    const int own = (nblk + p.partition_blocks - 1) / p.partition_blocks;   // 0 when L == 0
+    if (p.extra_count == 0 && own <= 1)
         return;                                // written directly by its only partition
+    // Partials to combine: the row's own partitions, then the shared-prefix ones.
+    const int nparts = own + p.extra_count;
+    auto slot = [&](int i) { return i < own ? i : p.extra_base + (i - own); };
     for (int h = wave; h < G; h += nw) {
         const int64_t row = (int64_t)s * Hq + (int64_t)kvh * G + h;
-        const int64_t base = row * NP;
+        const int64_t base = row * p.part_stride;
         float mx = -INFINITY;
         for (int i = lane; i < nparts; i += kWave)
-            mx = fmaxf(mx, p.part_max[base + i]);
+            mx = fmaxf(mx, p.part_max[base + slot(i)]);
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1)
             mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
         float tot = 0.0f;
         for (int i = lane; i < nparts; i += kWave)
-            tot += p.part_sum[base + i] * __builtin_amdgcn_exp2f((p.part_max[base + i] - mx) * kLog2e);
+            tot += p.part_sum[base + slot(i)] *
+                   __builtin_amdgcn_exp2f((p.part_max[base + slot(i)] - mx) * kLog2e);
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1)
             tot += __shfl_xor(tot, off, kWave);
@@ -653,20 +672,21 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams
             acc[e] = 0.0f;
         for (int c0 = 0; c0 < nparts; c0 += kWave) {
             const int i = c0 + lane;
-            wts[wave][lane] = i < nparts ? p.part_sum[base + i] *
-                                               __builtin_amdgcn_exp2f((p.part_max[base + i] - mx) * kLog2e)
+            wts[wave][lane] = i < nparts ? p.part_sum[base + slot(i)] *
+                                               __builtin_amdgcn_exp2f((p.part_max[base + slot(i)] - mx) *
+                                                                      kLog2e)
                                          : 0.0f;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             const int n = min(kWave, nparts - c0);
-            const float* po = p.part_out + (base + c0) * D + lane;
 #pragma unroll 8
             for (int j = 0; j < n; ++j) {
                 const float w = wts[wave][j];
+                const float* po = p.part_out + (base + slot(c0 + j)) * D + lane;
 #pragma unroll
                 for (int e = 0; e < DPL; ++e)
-                    acc[e] = fmaf(w, po[j * D + e * kWave], acc[e]);
+                    acc[e] = fmaf(w, po[e * kWave], acc[e]);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();

@@ -12,6 +12,8 @@ constexpr int kWave = 64;        // CDNA wavefront width
 constexpr int kMaxWaves = 8;     // waves per decode workgroup (single pass)
 constexpr int kPartWaves = 4;    // waves per decode workgroup (partitioned)
 constexpr int kReduceThreads = 256;
+constexpr int kCascadeWaves = 4;          // 64 query rows per prefix workgroup
+constexpr int kCascadeChunkBlocks = 32;   // prefix blocks per prefix workgroup
 
 // Element tags for the KV dtype.
 struct BF16 {
@@ -38,25 +40,34 @@ struct DecodeParams {
     int num_kv_heads;
     int group;                     // Hq / Hkv
     int partition_blocks;          // blocks per partition (single pass: >= MB)
-    int num_partitions;            // NP, the workspace stride
+    int num_partitions;            // partitions a context may span (longer ones are unreadable)
+    int part_stride;               // partial slots per row in the workspace (>= num_partitions)
     int num_seqs;
     int persistent;                // 1: persistent schedule over the items that exist
+    int skip_blocks;               // leading table entries that are not part of this call
+    int table_blocks;              // max_blocks_per_seq - skip_blocks
+    int partials_only;             // 1: write partials for every partition, never `out`
     float scale_log2;              // scale * log2(e)
 };
 
 struct ReduceParams {
     const int32_t* context_lens;
-    const float* part_max;         // [S][Hq][NP], natural-log units
-    const float* part_sum;         // [S][Hq][NP]
-    const float* part_out;         // [S][Hq][NP][D]
+    const float* part_max;         // [S][Hq][part_stride], natural-log units
+    const float* part_sum;         // [S][Hq][part_stride]
+    const float* part_out;         // [S][Hq][part_stride][D]
     void* out;                     // [S][Hq][D]
     int64_t num_blocks;
     int max_blocks_per_seq;
     int num_q_heads;
     int num_kv_heads;
     int group;
-    int num_partitions;
+    int num_partitions;            // as in DecodeParams
+    int part_stride;
     int partition_blocks;
+    int skip_blocks;
+    int table_blocks;
+    int extra_base;                // shared-prefix partials sit in slots [extra_base,
+    int extra_count;               //   extra_base + extra_count) of every row (cascade)
 };
 
 struct CacheParams {
@@ -114,6 +125,27 @@ constexpr size_t persistent_lds_bytes(int num_seqs) {
     return sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1 + 2 * kItemListCap);
 }
 
+// Shared-prefix (cascade) attention over the blocks every sequence shares.
+struct CascadeParams {
+    const void* q;                 // [S][Hq][D] bf16
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;   // the prefix ids are row 0's first num_prefix_blocks entries
+    float* part_max;               // workspace partials, row stride part_stride
+    float* part_sum;
+    float* part_out;
+    int64_t num_blocks;
+    int num_prefix_blocks;
+    int chunk_blocks;              // prefix blocks per workgroup
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int group;
+    int part_stride;               // row stride of the partials
+    int slot_base;                 // slot of prefix chunk 0
+    float scale_log2;
+};
+
 struct CopyParams {
     uint8_t* key_cache;
     uint8_t* value_cache;
@@ -129,5 +161,7 @@ hipError_t launch_reduce(const ReduceParams& p, int head_size, int out_bf16, int
                          hipStream_t stream);
 hipError_t launch_cache(const CacheParams& p, int64_t num_tokens, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, int64_t num_pairs, hipStream_t stream);
+hipError_t launch_cascade_prefix(const CascadeParams& p, int head_size, int num_chunks,
+                                 hipStream_t stream);
 
 }  // namespace pa

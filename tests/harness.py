@@ -94,8 +94,10 @@ def gpu_step(w: Workload, partition_size: Optional[int] = None, out_dtype=torch.
              in_place: bool = False, max_context_len: Optional[int] = None,
              block_tables: Optional[torch.Tensor] = None,
              context_lens: Optional[torch.Tensor] = None,
-             scatter: bool = True) -> GpuResult:
-    """Cache write then decode on the GPU through the C-ABI binding."""
+             scatter: bool = True, prefix_blocks: Optional[int] = None) -> GpuResult:
+    """Cache write then decode on the GPU through the C-ABI binding: pa_decode without a
+    partition size, pa_decode_partitioned with one, pa_decode_cascade (partition size
+    512 unless given) when prefix_blocks is set."""
     bt, cl, slots = device_inputs(w)
     if block_tables is not None:
         bt = block_tables
@@ -108,7 +110,13 @@ def gpu_step(w: Workload, partition_size: Optional[int] = None, out_dtype=torch.
     S, Hq, D = w.query.shape
     out = torch.empty((S, Hq, D), dtype=out_dtype, device=kc.device)
     ws = None
-    if partition_size is None:
+    if prefix_blocks is not None:
+        mcl = w.max_context_len if max_context_len is None else max_context_len
+        psize = 512 if partition_size is None else partition_size
+        ws = pa.cascade_workspace(S, Hq, D, mcl, psize, prefix_blocks, device=kc.device)
+        ws.fill_(0xFF)                  # NaN bit patterns: the call must not depend on them
+        pa.pa_decode_cascade(out, w.query, kc, vc, bt, cl, w.scale, prefix_blocks, mcl, psize, ws)
+    elif partition_size is None:
         pa.pa_decode(out, w.query, kc, vc, bt, cl, w.scale)
     else:
         mcl = w.max_context_len if max_context_len is None else max_context_len

@@ -151,3 +151,41 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         pa.pa_reshape_and_cache(x, x, x.view(1, 1, 1, 64), x.view(1, 1, 1, 64),
                                 torch.zeros(1, dtype=torch.int64))
+
+
+def cascade_call(lib, npb=2, max_ctx=37, psize=32, ws=P, ws_bytes=1 << 20, **kw):
+    a = decode_args(**{"kv_dt": 1, **kw})
+    return lib.pa_decode_cascade(a["out"], a["out_dt"], a["q"], a["kc"], a["vc"], a["kv_dt"],
+                                 a["bt"], a["MB"], a["cl"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                                 a["B"], a["NB"], a["scale"], npb, max_ctx, psize, ws, ws_bytes,
+                                 None)
+
+
+@pytest.mark.parametrize("kw,expect", [c for c in DECODE_CASES if "kv_dt" not in c[0]])
+def test_cascade_shares_decode_checks(lib, kw, expect):
+    assert cascade_call(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(kv_dt=0), EUNSUP), (dict(npb=0), EINVAL), (dict(npb=-1), EINVAL), (dict(npb=4), EINVAL),
+    (dict(NB=0), EINVAL), (dict(psize=24), EINVAL), (dict(psize=0), EINVAL),
+    (dict(max_ctx=-1), EINVAL), (dict(ws=0), EWS), (dict(ws_bytes=100), EWS),
+    (dict(ws=P + 16), EINVAL), (dict(max_ctx=16 * 70000, psize=16), EUNSUP),
+    (dict(S=0, ws=0, ws_bytes=0), OK),
+    (dict(npb=3, MB=3, ws=0), EWS),     # all blocks prefix is a valid shape
+])
+def test_cascade_checks(lib, kw, expect):
+    assert cascade_call(lib, **kw) == expect
+
+
+def test_cascade_workspace_size_formula(lib):
+    a256 = lambda n: (n + 255) // 256 * 256
+    for S, Hq, D, L, Ps, npb in [(128, 32, 128, 2560, 512, 128), (4, 4, 64, 37, 32, 1),
+                                 (3, 8, 64, 32, 16, 2), (1, 1, 128, 0, 16, 33),
+                                 (2, 16, 128, 5000, 256, 64)]:
+        sp = max(1, -(-max(L - 16 * npb, 0) // Ps))
+        R = S * Hq * (sp + -(-npb // 32))
+        assert pa.pa_decode_cascade_workspace_size(S, Hq, D, L, Ps, npb) == \
+            2 * a256(4 * R) + a256(4 * R * D)
+    assert pa.pa_decode_cascade_workspace_size(4, 4, 64, 10, 16, 0) == 0
+    assert pa.pa_decode_cascade_workspace_size(4, 4, 64, 10, 0, 1) == 0
