@@ -71,6 +71,14 @@ __device__ __forceinline__ float bf16_value(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
+// Workgroup barrier that orders LDS traffic only: global loads in flight
+// (the next step's K and V) stay in flight across it.
+__device__ __forceinline__ void wave_lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int D>
 __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(CascadeParams p) {
     constexpr int ROW = D * 2;                  // bytes per token row (bf16)
@@ -78,6 +86,10 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
     constexpr int CH = ROW / 16;                // 16-byte chunks per row
     constexpr int NQ = CH / 4;                  // K chunks per lane per tile
     constexpr int NT = D / 16;                  // 16-column output tiles
+    constexpr int VITEMS = (kStepTokens / 2) * CH;   // (token pair, chunk) items of a step
+    static_assert(VITEMS <= kCascadeWaves * kWave && (kCascadeWaves * kWave) % VITEMS == 0,
+                  "one V item per thread");
+    static_assert(kCascadeChunkBlocks <= kWave, "a chunk's block ids fit one per lane");
 
     __shared__ __attribute__((aligned(16))) uint16_t vt[D][kVtStride];
     __shared__ __attribute__((aligned(16))) float pl[kCascadeWaves][16][kPStride];
@@ -106,13 +118,43 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
                          : u32x4{0u, 0u, 0u, 0u};
     }
 
-    typedef __attribute__((address_space(4))) const int32_t ctable_t;
-    ctable_t* ids = (ctable_t*)p.block_tables;   // row 0 holds the shared prefix
+    // The chunk's prefix block ids (row 0 of the tables), one per lane. An id
+    // outside the pool poisons the chunk (NaN partials) and is read as block 0.
+    const int cb0 = chunk * p.chunk_blocks;
+    const int nblk = min(p.chunk_blocks, p.num_prefix_blocks - cb0);
+    int id_l = lane < nblk ? p.block_tables[cb0 + lane] : 0;
+    const bool bad_l = id_l < 0 || static_cast<int64_t>(id_l) >= p.num_blocks;
+    const bool poisoned = __ballot(bad_l) != 0;
+    id_l = bad_l ? 0 : id_l;
+    const int nsteps = (nblk + 1) / 2;
+
     const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE;
     const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE;
     const int64_t blk_stride = (int64_t)Hkv * TILE;
-    const int cb0 = chunk * p.chunk_blocks;
-    const int cb1 = min(cb0 + p.chunk_blocks, p.num_prefix_blocks);
+    // V item of this thread: token pair tp (tokens 2tp, 2tp + 1 of the step), chunk vc.
+    const int vi = threadIdx.x % VITEMS;
+    const int tp = vi % (kStepTokens / 2), vc = vi / (kStepTokens / 2);
+    const int vblk = tp >> 3;                   // which block of the step
+    const int voff = (2 * tp - 16 * vblk) * ROW + vc * 16;
+
+    // Loads of step st: the K tiles of its two blocks (a lone last block is
+    // read twice and masked) in the B-operand layout, and this thread's V pair.
+    u32x4 kt[2][NQ], vr[2];
+    auto load_step = [&](int st) {
+        const int b0 = 2 * st, b1 = min(2 * st + 1, nblk - 1);
+        const int id0 = __builtin_amdgcn_readlane(id_l, b0);
+        const int id1 = __builtin_amdgcn_readlane(id_l, b1);
+        const char* k0 = kbase + (int64_t)id0 * blk_stride + r16 * ROW + g * 16;
+        const char* k1 = kbase + (int64_t)id1 * blk_stride + r16 * ROW + g * 16;
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            kt[0][c] = *reinterpret_cast<const u32x4*>(k0 + 64 * c);
+            kt[1][c] = *reinterpret_cast<const u32x4*>(k1 + 64 * c);
+        }
+        const char* v = vbase + (int64_t)(vblk ? id1 : id0) * blk_stride + voff;
+        vr[0] = *reinterpret_cast<const u32x4*>(v);
+        vr[1] = *reinterpret_cast<const u32x4*>(v + ROW);
+    };
 
     float m[4], lsum[4];
     f32x4 o[NT];
@@ -124,57 +166,43 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
 #pragma unroll
     for (int n = 0; n < NT; ++n)
         o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    bool poisoned = false;
 
-    for (int jb = cb0; jb < cb1; jb += 2) {
-        const int nb = min(2, cb1 - jb);
-        int id[2];
-        id[0] = ids[jb];
-        id[1] = ids[jb + nb - 1];               // a lone last block is read twice, masked below
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if (id[b] < 0 || static_cast<int64_t>(id[b]) >= p.num_blocks) {
-                poisoned = true;
-                id[b] = 0;
-            }
-        }
-        // K tiles in the B-operand layout: lane = token r16, chunks g + 4c.
-        u32x4 kt[2][NQ];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const char* kp = kbase + (int64_t)id[b] * blk_stride + r16 * ROW + g * 16;
-#pragma unroll
-            for (int c = 0; c < NQ; ++c)
-                kt[b][c] = *reinterpret_cast<const u32x4*>(kp + 64 * c);
-        }
-        // V of the step's 32 tokens, transposed into LDS by the whole workgroup.
-        for (int idx = threadIdx.x; idx < kStepTokens * CH; idx += blockDim.x) {
-            const int t = idx / CH, c = idx - (idx / CH) * CH;
-            const int vid = (t >> 4) ? id[1] : id[0];
-            const u32x4 v = *reinterpret_cast<const u32x4*>(
-                vbase + (int64_t)vid * blk_stride + (t & 15) * ROW + c * 16);
+    load_step(0);
+    for (int st = 0; st < nsteps; ++st) {
+        const bool pair = 2 * st + 1 < nblk;
+        // V of the step, transposed into LDS: two adjacent tokens per 32-bit word.
+        {
+            uint32_t* col = reinterpret_cast<uint32_t*>(&vt[vc * 8][2 * tp]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                vt[c * 8 + 2 * e][t] = static_cast<uint16_t>(v[e] & 0xFFFFu);
-                vt[c * 8 + 2 * e + 1][t] = static_cast<uint16_t>(v[e] >> 16);
+                const uint32_t a = vr[0][e], b = vr[1][e];
+                col[(2 * e) * (kVtStride / 2)] = (a & 0xFFFFu) | (b << 16);
+                col[(2 * e + 1) * (kVtStride / 2)] = (a >> 16) | (b & 0xFFFF0000u);
             }
         }
+        u32x4 k0[NQ], k1[NQ];
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            k0[c] = kt[0][c];
+            k1[c] = kt[1][c];
+        }
+        // Next step's loads go out now and land while this step computes (the
+        // last step reloads itself, so that no load sits under a branch).
+        load_step(min(st + 1, nsteps - 1));
         // logits[row 4g+j][token b*16 + r16]
-        f32x4 acc[2];
+        f32x4 acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int c = 0; c < NQ; ++c)
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
-                                                                 __builtin_bit_cast(bf16x8, kt[b][c]),
-                                                                 acc[b], 0, 0, 0);
+        for (int c = 0; c < NQ; ++c) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
+                                                           __builtin_bit_cast(bf16x8, k0[c]), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
+                                                           __builtin_bit_cast(bf16x8, k1[c]), acc1, 0, 0, 0);
         }
         float alpha[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float x0 = acc[0][j] * p.scale_log2;
-            const float x1 = nb > 1 ? acc[1][j] * p.scale_log2 : -INFINITY;
+            const float x0 = acc0[j] * p.scale_log2;
+            const float x1 = pair ? acc1[j] * p.scale_log2 : -INFINITY;
             const float mn = fmaxf(m[j], row_max16(fmaxf(x0, x1)));
             alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
             const float p0 = __builtin_amdgcn_exp2f(x0 - mn);
@@ -189,7 +217,7 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 o[n][j] *= alpha[j];
-        __syncthreads();                        // P of every wave and all of V^T are in LDS
+        wave_lds_barrier();                     // P of every wave and all of V^T are in LDS
         // P as the A operand (row r16, tokens 8g..8g+7), split into bf16 hi + lo.
         u16x8 phi, plo;
         {
@@ -211,7 +239,7 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
             o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo),
                                                            __builtin_bit_cast(bf16x8, vb), o[n], 0, 0, 0);
         }
-        __syncthreads();                        // LDS free for the next step
+        wave_lds_barrier();                     // LDS free for the next step
     }
 
     // Row partials of this chunk: rows 4g+j of the wave, columns n*16 + r16.

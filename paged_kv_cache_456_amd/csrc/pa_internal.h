@@ -13,7 +13,7 @@ constexpr int kMaxWaves = 8;     // waves per decode workgroup (single pass)
 constexpr int kPartWaves = 4;    // waves per decode workgroup (partitioned)
 constexpr int kReduceThreads = 256;
 constexpr int kCascadeWaves = 4;          // 64 query rows per prefix workgroup
-constexpr int kCascadeChunkBlocks = 32;   // prefix blocks per prefix workgroup
+constexpr int kCascadeChunkBlocks = 16;   // prefix blocks per prefix workgroup
 
 // Element tags for the KV dtype.
 struct BF16 {
