@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for paged decode attention and the KV-cache write.
+"""fp64 CPU oracle for paged decode attention, multi-token queries over the paged
+cache, the KV-cache write and the copy-on-write block copy.
 
 TEST INFRASTRUCTURE ONLY. The test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` are the only callers. The GPU library never
@@ -70,6 +71,10 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
                                               ctypes.c_int64, ctypes.c_double, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int]
     lib.oracle_decode_partitioned.restype = ctypes.c_int
+    lib.oracle_prefill.argtypes = [dp, dp, dp, dp, i32p, i32p, i32p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int64, ctypes.c_double, ctypes.c_int]
+    lib.oracle_prefill.restype = ctypes.c_int
     lib.oracle_copy_blocks.argtypes = [u8p, u8p, i64p, ctypes.c_int64, ctypes.c_int64,
                                         ctypes.c_int64]
     lib.oracle_copy_blocks.restype = ctypes.c_int
@@ -221,3 +226,35 @@ def decode_partitioned(query, key_cache, value_cache, block_tables, context_lens
         num_threads)
     _check(rc)
     return out, pm, ps, po
+
+
+def prefill(query, key_cache, value_cache, block_tables, context_lens, query_start, scale: float,
+            num_threads: int = 0, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Multi-token queries over the paged cache in fp64. Returns out [T, Hq, D] (float64).
+
+    query [T, Hq, D] with T = query_start[-1]; query_start [S + 1] int32 (0, then
+    non-decreasing): the rows of sequence s are query_start[s] .. query_start[s + 1] - 1, the
+    last q_s tokens of its context, and row i attends causally to tokens
+    0 .. context_lens[s] - q_s + i.
+    """
+    lib = lib or _lib()
+    q = _f64(query)
+    kc = _f64(key_cache)
+    vc = _f64(value_cache)
+    bt = _i32(block_tables)
+    cl = _i32(context_lens)
+    qs = _i32(query_start)
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = kc.shape
+    S = cl.shape[0]
+    if D2 != D or vc.shape != kc.shape or bt.shape[0] != S or qs.shape != (S + 1,) or \
+            (S > 0 and int(qs[-1]) != T):
+        raise ValueError("shapes disagree")
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    rc = lib.oracle_prefill(_ptr(out, ctypes.c_double), _ptr(q, ctypes.c_double),
+                            _ptr(kc, ctypes.c_double), _ptr(vc, ctypes.c_double),
+                            _ptr(bt, ctypes.c_int32), _ptr(cl, ctypes.c_int32),
+                            _ptr(qs, ctypes.c_int32), S, Hq, Hkv, D, B, bt.shape[1], NB,
+                            fp32_scale(scale), num_threads)
+    _check(rc)
+    return out

@@ -1,6 +1,7 @@
 /*
- * pa_oracle.c -- plain fp64 CPU oracle for paged KV-cache decode attention
- * and for the KV-cache write.
+ * pa_oracle.c -- plain fp64 CPU oracle for paged KV-cache decode attention,
+ * multi-token queries over the paged cache, the KV-cache write and the
+ * copy-on-write block copy.
  *
  * TEST INFRASTRUCTURE ONLY. The test suite, the package smoke check and the
  * CPU-baseline leg of the benchmark are the only code that may load this
@@ -40,6 +41,14 @@
  *    s_p = sum exp(l_t - m_p) and normalised output o_p, and the partitions
  *    are combined with log-sum-exp weights s_p * exp(m_p - M), M = max m_p.
  *    In exact arithmetic this equals the single-pass result.
+ *
+ *  - Multi-token queries (a reading). "Problem 1" on "vLLM Solved the Wrong
+ *    Bottleneck" walks through a 1000-token prompt followed by generated
+ *    tokens, each of which attends to all tokens before it. Sequence s brings
+ *    q_s new tokens, the last q_s of its L_s-token context (already written
+ *    to the cache); its query token i sits at position pos = L_s - q_s + i
+ *    and attends, causally, to tokens 0 .. pos with the same softmax
+ *    attention. q_s = 1 is the decode above.
  *
  *  - KV-cache write (a reading). Each new token i with slot_mapping[i] >= 0
  *    is copied byte for byte into row slot % B of block slot / B, for every
@@ -247,6 +256,91 @@ int oracle_decode(double* out, const double* query,
             }
         }
         free(K); free(V); free(l);
+    }
+    return failed ? ORACLE_NOMEM : ORACLE_OK;
+}
+
+/* Multi-token queries. query and out are [T][num_q_heads][head_size] with
+ * T = query_start[num_seqs]; the q_s = query_start[s + 1] - query_start[s]
+ * rows of sequence s start at row query_start[s]. Row i of sequence s is the
+ * query at context position L_s - q_s + i and attends to tokens 0 .. that
+ * position. Requires query_start[0] = 0, non-decreasing, and q_s <= L_s. */
+int oracle_prefill(double* out, const double* query,
+                   const double* key_cache, const double* value_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* query_start,
+                   int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
+                   int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                   double scale, int num_threads)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads != 0)
+        return ORACLE_BAD_ARG;
+    if (num_seqs > 0 && query_start[0] != 0)
+        return ORACLE_BAD_ARG;
+    for (int s = 0; s < num_seqs; ++s) {
+        const int nq = query_start[s + 1] - query_start[s];
+        if (nq < 0)
+            return ORACLE_BAD_ARG;
+        if (nq > context_lens[s])
+            return ORACLE_BAD_LEN;
+    }
+    int rc = check_tables(block_tables, context_lens, num_seqs, block_size,
+                          max_blocks_per_seq, num_blocks);
+    if (rc != ORACLE_OK)
+        return rc;
+
+    const int group = num_q_heads / num_kv_heads;
+    const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+    int failed = 0;
+#ifdef _OPENMP
+    if (num_threads > 0)
+        omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+    for (int64_t pr = 0; pr < pairs; ++pr) {
+        const int s = (int)(pr / num_kv_heads);
+        const int kv = (int)(pr % num_kv_heads);
+        const int L = context_lens[s];
+        const int nq = query_start[s + 1] - query_start[s];
+        if (nq == 0)
+            continue;
+        const int32_t* table_row = block_tables + (int64_t)s * max_blocks_per_seq;
+        double* K = (double*)malloc((size_t)L * head_size * sizeof(double));
+        double* V = (double*)malloc((size_t)L * head_size * sizeof(double));
+        double* e = (double*)malloc((size_t)L * sizeof(double));
+        if (!K || !V || !e) {
+            free(K); free(V); free(e);
+            failed = 1;
+            continue;
+        }
+        gather_head(K, key_cache, table_row, L, kv, num_kv_heads, block_size, head_size);
+        gather_head(V, value_cache, table_row, L, kv, num_kv_heads, block_size, head_size);
+
+        for (int i = 0; i < nq; ++i) {
+            const int pos = L - nq + i;            /* the query's own position */
+            const int64_t row = (int64_t)query_start[s] + i;
+            for (int hh = 0; hh < group; ++hh) {
+                const int head = kv * group + hh;
+                const double* qh = query + ((size_t)row * num_q_heads + head) * head_size;
+                double* o = out + ((size_t)row * num_q_heads + head) * head_size;
+                logits_range(e, qh, K, 0, pos + 1, head_size, scale);
+                double mx = -INFINITY;
+                for (int t = 0; t <= pos; ++t)
+                    mx = e[t] > mx ? e[t] : mx;
+                double sum = 0.0;
+                for (int t = 0; t <= pos; ++t) {
+                    e[t] = exp(e[t] - mx);
+                    sum += e[t];
+                }
+                for (int d = 0; d < head_size; ++d)
+                    o[d] = 0.0;
+                for (int t = 0; t <= pos; ++t)
+                    for (int d = 0; d < head_size; ++d)
+                        o[d] += e[t] / sum * V[(size_t)t * head_size + d];
+            }
+        }
+        free(K); free(V); free(e);
     }
     return failed ? ORACLE_NOMEM : ORACLE_OK;
 }

@@ -431,4 +431,140 @@ def pin_copy_blocks_rejects(lib):
         raise AssertionError(f"pairs {pairs} accepted")
 
 
+# --------------------------------------------------------------------------
+# Multi-token queries (a prompt chunk per sequence) over the paged cache
+# --------------------------------------------------------------------------
+
+def prefill_problem(rng, lengths, nqs, Hq, Hkv, D, scale=None, poison=True):
+    """random_problem plus a ragged batch of query rows: sequence s brings nqs[s] rows."""
+    p = random_problem(rng, lengths, Hq, Hkv, D, scale=scale, poison=poison)
+    p["qs"] = np.concatenate([[0], np.cumsum(nqs)]).astype(np.int32)
+    p["nq"] = list(nqs)
+    p["qm"] = rng.standard_normal((int(p["qs"][-1]), Hq, D))
+    return p
+
+
+def run_prefill(lib, p, **kw):
+    return oracle.prefill(p["qm"], p["kc"], p["vc"], p["bt"], p["cl"], p["qs"], p["scale"],
+                          lib=lib, **kw)
+
+
+def pin_prefill_sdpa_causal(lib):
+    """Multi-token queries == torch SDPA (fp64, CPU) with an explicit boolean mask: query i
+    of a q-token chunk sees tokens 0 .. L - q + i of the contiguous cache."""
+    rng = np.random.default_rng(31)
+    lengths, nqs = [1, 7, 16, 33, 50, 40], [1, 7, 5, 16, 50, 0]
+    Hq, Hkv, D = 8, 2, 24
+    p = prefill_problem(rng, lengths, nqs, Hq, Hkv, D, scale=0.3)
+    out = run_prefill(lib, p)
+    sc = oracle.fp32_scale(p["scale"])
+    for s, (L, nq) in enumerate(zip(lengths, nqs)):
+        if nq == 0:
+            continue
+        r0 = int(p["qs"][s])
+        q = torch.from_numpy(p["qm"][r0:r0 + nq]).permute(1, 0, 2).reshape(1, Hq, nq, D)
+        k = torch.from_numpy(p["Ks"][s]).permute(1, 0, 2).reshape(1, Hkv, L, D)
+        v = torch.from_numpy(p["Vs"][s]).permute(1, 0, 2).reshape(1, Hkv, L, D)
+        k = k.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+        v = v.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+        mask = torch.arange(L)[None, :] <= (L - nq + torch.arange(nq))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=sc)
+        ref = ref.reshape(Hq, nq, D).permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(out[r0:r0 + nq], ref, rtol=0, atol=1e-12)
+
+
+def pin_prefill_rows_are_truncated_decodes(lib):
+    """Row i of a chunk is the single-query decode of the same context cut at the row's
+    position (context length L - q + i + 1), query for query."""
+    rng = np.random.default_rng(32)
+    lengths, nqs = [5, 20, 48, 17], [5, 3, 33, 1]
+    Hq, Hkv, D = 6, 3, 16
+    p = prefill_problem(rng, lengths, nqs, Hq, Hkv, D)
+    out = run_prefill(lib, p)
+    for s, (L, nq) in enumerate(zip(lengths, nqs)):
+        r0 = int(p["qs"][s])
+        for i in range(nq):
+            dec = oracle.decode(p["qm"][r0 + i][None], p["kc"], p["vc"], p["bt"][s][None],
+                                np.array([L - nq + i + 1], np.int32), p["scale"], lib=lib)
+            np.testing.assert_allclose(out[r0 + i], dec[0], rtol=0, atol=1e-12)
+
+
+def pin_prefill_brute_force(lib):
+    """A scalar Python loop (no max shift, math.fsum) over the causal window, tiny inputs."""
+    rng = np.random.default_rng(33)
+    lengths, nqs = [3, 18, 9], [3, 4, 2]
+    Hq, Hkv, D = 4, 2, 3
+    p = prefill_problem(rng, lengths, nqs, Hq, Hkv, D, scale=0.7)
+    out = run_prefill(lib, p)
+    sc = oracle.fp32_scale(p["scale"])
+    G = Hq // Hkv
+    for s, (L, nq) in enumerate(zip(lengths, nqs)):
+        for i in range(nq):
+            row = int(p["qs"][s]) + i
+            pos = L - nq + i
+            for h in range(Hq):
+                kv = h // G
+                e = []
+                for t in range(pos + 1):
+                    b = p["bt"][s][t // B]
+                    e.append(math.exp(sc * math.fsum(p["qm"][row][h][d] * p["kc"][b][kv][t % B][d]
+                                                     for d in range(D))))
+                z = math.fsum(e)
+                for d in range(D):
+                    ref = math.fsum(e[t] / z * p["vc"][p["bt"][s][t // B]][kv][t % B][d]
+                                    for t in range(pos + 1))
+                    assert abs(out[row][h][d] - ref) < 1e-12, (s, i, h, d)
+
+
+def pin_prefill_first_prompt_token(lib):
+    """When the chunk is the whole prompt (q = L), its first row sees token 0 alone and
+    returns that token's V exactly; the others stay finite."""
+    rng = np.random.default_rng(34)
+    lengths = [1, 16, 37]
+    Hq, Hkv, D = 4, 4, 8
+    p = prefill_problem(rng, lengths, lengths, Hq, Hkv, D)
+    out = run_prefill(lib, p)
+    for s, L in enumerate(lengths):
+        r0 = int(p["qs"][s])
+        v0 = p["Vs"][s][0]                                   # [Hkv, D]
+        assert np.array_equal(out[r0], v0), s
+        assert np.isfinite(out[r0:r0 + L]).all()
+
+
+def pin_prefill_causality(lib):
+    """Changing the K and V of a context's last token changes only the row at that position
+    (bit for bit: the earlier rows never read it)."""
+    rng = np.random.default_rng(35)
+    lengths, nqs = [30, 45], [12, 45]
+    Hq, Hkv, D = 4, 2, 8
+    p = prefill_problem(rng, lengths, nqs, Hq, Hkv, D)
+    base = run_prefill(lib, p)
+    for s, L in enumerate(lengths):
+        q = dict(p)
+        q["kc"], q["vc"] = p["kc"].copy(), p["vc"].copy()
+        b, off = p["bt"][s][(L - 1) // B], (L - 1) % B
+        q["kc"][b, :, off] += 3.0
+        q["vc"][b, :, off] -= 5.0
+        moved = run_prefill(lib, q)
+        last = int(p["qs"][s + 1]) - 1
+        changed = np.flatnonzero(np.any(moved != base, axis=(1, 2)))
+        assert changed.tolist() == [last], (s, changed)
+
+
+def pin_prefill_rejects(lib):
+    """A chunk longer than its context, or a query_start that does not start at 0 or runs
+    backwards, is an input error."""
+    rng = np.random.default_rng(36)
+    p = prefill_problem(rng, [5, 9], [2, 3], 2, 2, 4)
+    for qs in ([0, 6, 9], [1, 3, 6], [0, 3, 2]):
+        q = dict(p)
+        q["qs"] = np.asarray(qs, np.int32)
+        q["qm"] = np.zeros((max(qs[-1], 0), 2, 4))
+        try:
+            run_prefill(lib, q)
+        except oracle.OracleError:
+            continue
+        raise AssertionError(f"query_start {qs} accepted")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -31,11 +31,18 @@ MUTANTS = [
      "for (int t = 0; t < L - 1; ++t) {\n                const double w = l[t] / z;", 1),
     ("dot_term_dropped", "for (int d = 0; d < head_size; ++d)\n            dot +=",
      "for (int d = 1; d < head_size; ++d)\n            dot +=", 1),
-    ("v_from_k_pool", "gather_head(V, value_cache,", "gather_head(V, key_cache,", 2),
+    ("v_from_k_pool", "gather_head(V, value_cache,", "gather_head(V, key_cache,", 3),
     ("lse_sign", "const double w = sp[p] * exp(mp[p] - M);", "const double w = sp[p] * exp(M - mp[p]);", 1),
     ("partition_skips_token", "const int t0 = p * partition_size;",
      "const int t0 = p * partition_size + (p > 0);", 1),
     ("partition_unnormalised", "const double w = l[t] / sp[p];", "const double w = l[t];", 1),
+    ("prefill_pos_off_by_one", "const int pos = L - nq + i;", "const int pos = L - nq + i - 1;", 1),
+    ("prefill_pos_origin", "const int pos = L - nq + i;", "const int pos = i;", 1),
+    ("prefill_no_causal_mask", "const int pos = L - nq + i;", "const int pos = L - 1;", 1),
+    ("prefill_rows_reversed", "const int64_t row = (int64_t)query_start[s] + i;",
+     "const int64_t row = (int64_t)query_start[s] + (nq - 1 - i);", 1),
+    ("prefill_head_map", "const int head = kv * group + hh;",
+     "const int head = hh * num_kv_heads + kv;", 1),
     ("scatter_offset", "int64_t offset = slot % block_size;", "int64_t offset = slot / block_size;", 1),
     ("scatter_kv_swap", "memcpy(value_cache + dst, value + src, row);",
      "memcpy(value_cache + dst, key + src, row);", 1),
