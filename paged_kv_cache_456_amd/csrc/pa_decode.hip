@@ -193,13 +193,26 @@ __device__ __forceinline__ int call_len(int L, int skip_blocks) {
     return L < skip ? -1 : static_cast<int>(L - skip);
 }
 
-// One work item: the partition `part` of KV head `kvh` of sequence `s`
-// (context length L), computed by the whole workgroup. Writes the output row
-// directly when the context has a single partition, else the partition's
-// partials. All arguments are wave-uniform.
+// Writes the output rows of the head group of KV head `kvh` of sequence `s`
+// when its context has nothing to read: zeros for an empty context, NaN for
+// an unreadable one.
+template <typename OUT>
+__device__ __forceinline__ void fill_rows(const DecodeParams& p, int kvh, int s, int D, float v) {
+    const int G = p.group;
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+        const int h = idx / D, d = idx - (idx / D) * D;
+        store_out<OUT>(p.out, ((int64_t)s * p.num_q_heads + kvh * G + h) * D + d, v);
+    }
+}
+
+// Blocks [pb0, pb1) of the context of KV head `kvh` of sequence `s` (L > 0
+// tokens, readable), computed by the whole workgroup. With `direct` the range
+// is the whole context and the output row is written; otherwise the range's
+// (max, sum, normalised output) go to partial slot `slot` of the workspace.
+// All arguments are wave-uniform.
 template <typename KV, int D, int GMAX, typename OUT>
-__device__ __forceinline__ void process_item(const DecodeParams& p, float* smem, int kvh, int s,
-                                             int part, int L) {
+__device__ __forceinline__ void process_range(const DecodeParams& p, float* smem, int kvh, int s,
+                                              int L, int pb0, int pb1, int slot, bool direct) {
     using Gm = Geometry<KV, D>;
     using Op = Ops<KV>;
     constexpr int NQ = Gm::kNq, NV = Gm::kNv, CH = Gm::kCh, TPL = Gm::kTpl, EPC = Gm::kEpc;
@@ -213,24 +226,6 @@ __device__ __forceinline__ void process_item(const DecodeParams& p, float* smem,
     const int nw = blockDim.x / kWave;
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads, G = p.group;
 
-    const bool bad_len = context_unreadable(L, p.table_blocks, p.num_partitions,
-                                            p.partition_blocks, p.num_blocks);
-    if (bad_len || L == 0) {
-        if (part == 0 && !p.partials_only) {
-            const float fill = bad_len ? __builtin_nanf("") : 0.0f;
-            for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-                const int h = idx / D, d = idx - (idx / D) * D;
-                store_out<OUT>(p.out, ((int64_t)s * Hq + kvh * G + h) * D + d, fill);
-            }
-        }
-        return;
-    }
-    const int nblk = (L + kBlockSize - 1) / kBlockSize;
-    const int nparts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
-    const int pb0 = part * p.partition_blocks;
-    if (pb0 >= nblk)
-        return;
-    const int pb1 = min(pb0 + p.partition_blocks, nblk);
     const int tok_end = min(pb1 * kBlockSize, L);
     const int per_round = nw * BPW;
     const int rounds = (pb1 - pb0 + per_round - 1) / per_round;
@@ -488,7 +483,7 @@ __device__ __forceinline__ void process_item(const DecodeParams& p, float* smem,
     __syncthreads();
 
     // Merge the waves in a fixed order.
-    const bool split = nparts > 1 || p.partials_only;
+    const bool split = !direct;
     for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
         const int h = idx / D;
         const int d = idx - h * D;
@@ -505,7 +500,7 @@ __device__ __forceinline__ void process_item(const DecodeParams& p, float* smem,
         if (!split) {
             store_out<OUT>(p.out, row * D + d, acc / S);
         } else {
-            const int64_t pi = row * p.part_stride + part;
+            const int64_t pi = row * p.part_stride + slot;
             p.part_out[pi * D + d] = acc / S;
             if (d == 0) {
                 p.part_max[pi] = M * kLn2;
@@ -515,36 +510,60 @@ __device__ __forceinline__ void process_item(const DecodeParams& p, float* smem,
     }
 }
 
-// Work slots of a sequence in the persistent schedule: its partitions, or a
-// single slot (which writes the zero or NaN row) when there is nothing to read.
-__device__ __forceinline__ int sequence_slots(int L, const DecodeParams& p) {
+// Blocks a context spans, as the schedule counts them: a context with nothing
+// to read counts one block (its item writes the zero or NaN row).
+__device__ __forceinline__ int schedule_blocks(int L, const DecodeParams& p) {
     if (L == 0 || context_unreadable(L, p.table_blocks, p.num_partitions, p.partition_blocks,
                                      p.num_blocks))
         return 1;
-    const int nblk = (L + kBlockSize - 1) / kBlockSize;
-    return (nblk + p.partition_blocks - 1) / p.partition_blocks;
+    return (L + kBlockSize - 1) / kBlockSize;
 }
 
-// Grid mode (one workgroup per (KV head, sequence, partition), the single
-// pass included) or persistent mode: a grid no larger than what the GPU holds
-// at once, where workgroup w takes the items w, w + grid, w + 2 grid, ... of
-// the list of (sequence, partition, KV head) items that actually exist. The
-// list is built from context_lens in LDS, so no workgroup is spent on the
-// empty partitions of short sequences.
+// Partition `part` of the context of KV head `kvh` of sequence `s`.
+template <typename KV, int D, int GMAX, typename OUT>
+__device__ __forceinline__ void process_partition(const DecodeParams& p, float* smem, int kvh,
+                                                  int s, int L, int part) {
+    const bool bad = context_unreadable(L, p.table_blocks, p.num_partitions, p.partition_blocks,
+                                        p.num_blocks);
+    if (bad || L == 0) {
+        if (part == 0 && !p.partials_only)
+            fill_rows<OUT>(p, kvh, s, D, bad ? __builtin_nanf("") : 0.0f);
+        return;
+    }
+    const int nblk = (L + kBlockSize - 1) / kBlockSize;
+    const int PB = p.partition_blocks;
+    const int np = (nblk + PB - 1) / PB;
+    if (part >= np)
+        return;
+    process_range<KV, D, GMAX, OUT>(p, smem, kvh, s, L, part * PB, min((part + 1) * PB, nblk), part,
+                                    np == 1 && !p.partials_only);
+}
+
+// Grid schedule: one workgroup per (KV head, sequence, partition). The single
+// pass is the case of one partition spanning the whole table.
 template <typename KV, int D, int GMAX, typename OUT>
 __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeParams p) {
     extern __shared__ float smem[];
-    process_item<KV, D, GMAX, OUT>(p, smem, blockIdx.x, blockIdx.y, blockIdx.z,
-                                   call_len(p.context_lens[blockIdx.y], p.skip_blocks));
+    process_partition<KV, D, GMAX, OUT>(p, smem, blockIdx.x, blockIdx.y,
+                                        call_len(p.context_lens[blockIdx.y], p.skip_blocks),
+                                        blockIdx.z);
 }
 
-// Waves per SIMD the persistent kernel is register-allocated for: three
-// 4-wave workgroups per CU for head groups up to 4, two for larger ones.
+// Waves per SIMD the persistent kernel is register-allocated for: three 4-wave
+// workgroups per CU for head groups up to 4, two for larger ones.
 template <typename KV, int D, int GMAX>
 constexpr int persistent_waves_per_simd() {
     return (GMAX <= 4 && D * KV::kBytes <= 256) ? 3 : 2;
 }
 
+// Persistent schedule: a grid no larger than what the GPU holds at once,
+// where workgroup w takes the items w, w + W, w + 2W, ... of the list of
+// (sequence, partition, KV head) items that exist, KV head fastest. The list
+// is built from context_lens in LDS, so no workgroup is spent on the empty
+// partitions of short sequences. Dealing items round-robin in this order has
+// neighbouring workgroups read the same physical blocks for different KV
+// heads at about the same time (measured faster on MI355X than contiguous,
+// tile-balanced ranges, and than dealing KV head by KV head).
 template <typename KV, int D, int GMAX, typename OUT>
 __global__ __launch_bounds__(kPartWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(persistent_waves_per_simd<KV, D, GMAX>())))
@@ -554,7 +573,7 @@ void paged_decode_persistent_kernel(DecodeParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int S = p.num_seqs, Hkv = p.num_kv_heads;
     int* lens = reinterpret_cast<int*>(smem + decode_lds_floats(KV::kBytes, D, p.group, nw));
-    int* first_slot = lens + S;                 // [S + 1], exclusive prefix sum of slots
+    int* first_slot = lens + S;                 // [S + 1], exclusive prefix sum of partitions
     int* list = first_slot + S + 1;             // [kItemListCap][2]: sequence, part << 8 | kvh
     for (int i = threadIdx.x; i < S; i += blockDim.x)
         lens[i] = call_len(p.context_lens[i], p.skip_blocks);
@@ -563,7 +582,8 @@ void paged_decode_persistent_kernel(DecodeParams p) {
         int carry = 0;
         for (int c0 = 0; c0 < S; c0 += kWave) {
             const int i = c0 + lane;
-            const int v = i < S ? sequence_slots(lens[i], p) : 0;
+            const int nb = i < S ? schedule_blocks(lens[i], p) : 0;
+            const int v = (nb + p.partition_blocks - 1) / p.partition_blocks;
             int incl = v;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
@@ -607,8 +627,8 @@ void paged_decode_persistent_kernel(DecodeParams p) {
             if (seq < 0)
                 break;
             const int pk = __builtin_amdgcn_readfirstlane(list[2 * k + 1]);
-            process_item<KV, D, GMAX, OUT>(p, smem, pk & 0xFF, seq, pk >> 8,
-                                           __builtin_amdgcn_readfirstlane(lens[seq]));
+            process_partition<KV, D, GMAX, OUT>(p, smem, pk & 0xFF, seq,
+                                                __builtin_amdgcn_readfirstlane(lens[seq]), pk >> 8);
             __syncthreads();                        // the item's LDS is free again
         }
         __syncthreads();                            // every thread is done with this list
@@ -616,16 +636,19 @@ void paged_decode_persistent_kernel(DecodeParams p) {
 }
 
 // Log-sum-exp combination of the partitions of every (sequence, KV head)
-// whose context spans more than one partition: one workgroup per pair, one
-// wave per query head at a time. The wave loads the head's partition maxima
-// and sums lane-parallel, reduces them to the weights
-//     w_p = s_p exp(m_p - M) / sum_q s_q exp(m_q - M),  M = max_p m_p,
-// stages the weights in LDS, and accumulates sum_p w_p o_p over the partition
-// outputs with independent loads. All reductions run in a fixed order.
+// whose context spans more than one partition: one workgroup per row, one
+// wave per query head at a time. The row's partials are its own partitions
+// followed by any extra slots (shared-prefix chunks), merged 64 at a time:
+//     M = max_i m_i,  w_i = s_i exp(m_i - M),  out = sum_i w_i o_i / sum_i w_i,
+// the running sums rescaled when a later batch raises M. The loads of a batch
+// (maxima, sums and the output rows of up to 16 partials) are all issued
+// before any of them is used; further output rows follow 16 at a time. All
+// reductions run in a fixed order.
 template <int D, typename OUT>
 __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams p) {
     constexpr int DPL = D / kWave;              // output elements per lane
-    __shared__ float wts[kReduceThreads / kWave][kWave];
+    constexpr int PRE = 16;                     // partial outputs loaded together
+    __shared__ int slots[kReduceThreads / kWave][kWave];
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
@@ -635,7 +658,7 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams
     const int L = call_len(p.context_lens[s], p.skip_blocks);
     const bool bad = context_unreadable(L, p.table_blocks, NP, p.partition_blocks, p.num_blocks);
     if (p.extra_count == 0 && (bad || L == 0))
-        return;                                // the partition kernel wrote this row
+        return;                                // the decode kernel wrote this row
     if (bad) {                                 // cascade: an unreadable suffix
         for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
             const int h = idx / D, d = idx - (idx / D) * D;
@@ -647,54 +670,87 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams
     const int own = (nblk + p.partition_blocks - 1) / p.partition_blocks;   // 0 when L == 0
     if (p.extra_count == 0 && own <= 1)
         return;                                // written directly by its only partition
-    // Partials to combine: the row's own partitions, then the shared-prefix ones.
-    const int nparts = own + p.extra_count;
-    auto slot = [&](int i) { return i < own ? i : p.extra_base + (i - own); };
+    const int total = own + p.extra_count;     // partial slots: own partitions, then extras
     for (int h = wave; h < G; h += nw) {
         const int64_t row = (int64_t)s * Hq + (int64_t)kvh * G + h;
         const int64_t base = row * p.part_stride;
-        float mx = -INFINITY;
-        for (int i = lane; i < nparts; i += kWave)
-            mx = fmaxf(mx, p.part_max[base + slot(i)]);
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1)
-            mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-        float tot = 0.0f;
-        for (int i = lane; i < nparts; i += kWave)
-            tot += p.part_sum[base + slot(i)] *
-                   __builtin_amdgcn_exp2f((p.part_max[base + slot(i)] - mx) * kLog2e);
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1)
-            tot += __shfl_xor(tot, off, kWave);
+        float M = -INFINITY, T = 0.0f;
         float acc[DPL];
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
             acc[e] = 0.0f;
-        for (int c0 = 0; c0 < nparts; c0 += kWave) {
+        for (int c0 = 0; c0 < total; c0 += kWave) {
             const int i = c0 + lane;
-            wts[wave][lane] = i < nparts ? p.part_sum[base + slot(i)] *
-                                               __builtin_amdgcn_exp2f((p.part_max[base + slot(i)] - mx) *
-                                                                      kLog2e)
-                                         : 0.0f;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int n = min(kWave, nparts - c0);
-#pragma unroll 8
-            for (int j = 0; j < n; ++j) {
-                const float w = wts[wave][j];
-                const float* po = p.part_out + (base + slot(c0 + j)) * D + lane;
+            const int n = min(kWave, total - c0);
+            slots[wave][lane] = i < own ? i : p.extra_base + (i - own);
+            wave_lds_sync();
+            // Lane j < n holds partial j's statistics; the first PRE outputs are
+            // requested together with them.
+            const int my = lane < n ? slots[wave][lane] : 0;
+            const float mv = lane < n ? p.part_max[base + my] : -INFINITY;
+            const float sv = lane < n ? p.part_sum[base + my] : 0.0f;
+            float ov[PRE][DPL];
+#pragma unroll
+            for (int j = 0; j < PRE; ++j) {
+                // Past the batch's partials the load re-reads slot 0 of the row
+                // (always inside the workspace); the value is not used.
+                const int sj = j < n ? slots[wave][j] : 0;
+                const float* po = p.part_out + (base + sj) * D + lane;
 #pragma unroll
                 for (int e = 0; e < DPL; ++e)
-                    acc[e] = fmaf(w, po[e * kWave], acc[e]);
+                    ov[j][e] = po[e * kWave];
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float cm = mv;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1)
+                cm = fmaxf(cm, __shfl_xor(cm, o, kWave));
+            const float Mn = fmaxf(M, cm);
+            const float scale = M == Mn ? 1.0f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
+            const float wv = lane < n ? sv * __builtin_amdgcn_exp2f((mv - Mn) * kLog2e) : 0.0f;
+            float ws = wv;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1)
+                ws += __shfl_xor(ws, o, kWave);
+            T = T * scale + ws;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                acc[e] *= scale;
+#pragma unroll
+            for (int j = 0; j < PRE; ++j) {
+                if (j < n) {
+                    const float w = readlane_f(wv, j);
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e)
+                        acc[e] = fmaf(w, ov[j][e], acc[e]);
+                }
+            }
+            // The batch's remaining partials, PRE at a time, each group's
+            // loads in flight together.
+            for (int j0 = PRE; j0 < n; j0 += PRE) {
+#pragma unroll
+                for (int j = 0; j < PRE; ++j) {
+                    const int sj = j0 + j < n ? slots[wave][j0 + j] : 0;
+                    const float* po = p.part_out + (base + sj) * D + lane;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e)
+                        ov[j][e] = po[e * kWave];
+                }
+#pragma unroll
+                for (int j = 0; j < PRE; ++j) {
+                    if (j0 + j < n) {
+                        const float w = readlane_f(wv, j0 + j);
+#pragma unroll
+                        for (int e = 0; e < DPL; ++e)
+                            acc[e] = fmaf(w, ov[j][e], acc[e]);
+                    }
+                }
+            }
+            M = Mn;
+            wave_lds_sync();
         }
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
-            store_out<OUT>(p.out, row * D + lane + e * kWave, acc[e] / tot);
+            store_out<OUT>(p.out, row * D + lane + e * kWave, acc[e] / T);
     }
 }
 

@@ -43,7 +43,7 @@ struct DecodeParams {
     int num_partitions;            // partitions a context may span (longer ones are unreadable)
     int part_stride;               // partial slots per row in the workspace (>= num_partitions)
     int num_seqs;
-    int persistent;                // 1: persistent schedule over the items that exist
+    int persistent;                // 1: persistent schedule (resident grid), 0: one workgroup per partition
     int skip_blocks;               // leading table entries that are not part of this call
     int table_blocks;              // max_blocks_per_seq - skip_blocks
     int partials_only;             // 1: write partials for every partition, never `out`

@@ -130,11 +130,10 @@ def test_partials_match_oracle():
     assert checked == 2
 
 
-def test_balanced_schedule_cuts_partitions():
-    """One long context among short ones: the balanced schedule cuts its partitions into
-    pieces across workgroups; outputs and per-partition partials still match the oracle,
-    also with one sequence only, with empty and unreadable contexts in the batch, and for
-    partitions larger than a workgroup's share."""
+def test_partitioned_mixed_lengths():
+    """One long context among short ones, one sequence only, tiny partitions, and
+    partitions longer than most contexts: outputs and per-partition partials match the
+    oracle; also with empty and unreadable contexts in the batch."""
     for lengths, psize in (([8000, 3, 40, 1, 700], 512), ([20000], 2048), ([1, 2, 3], 16),
                            ([4096] * 3 + [1] * 40, 4096)):
         spec = wl.custom_spec(lengths, 8, 2, 128, torch.bfloat16, index=310 + len(lengths))
@@ -160,6 +159,21 @@ def test_balanced_schedule_cuts_partitions():
     g = gpu_step(w, partition_size=32, context_lens=cl_bad)
     _report("balanced with empty rows", max_abs_err(g.out[:4], r.out), TOL[torch.bfloat16])
     assert torch.equal(g.out[0], torch.zeros_like(g.out[0])) and torch.isnan(g.out[4]).all()
+
+
+def test_reduce_many_partitions():
+    """Rows with more than 16 and more than 64 partitions: the combining kernel loads
+    partials 16 at a time and merges them 64 at a time with rescaling; both must give
+    the single-pass result (fp32 and bf16 KV)."""
+    for lengths, hq, hkv, d, dt, psize in (([3000, 1100, 17, 300], 8, 2, 128, torch.bfloat16, 16),
+                                           ([2100, 40], 4, 4, 64, torch.float32, 32),
+                                           ([1040, 5], 8, 1, 128, torch.bfloat16, 16)):
+        spec = wl.custom_spec(lengths, hq, hkv, d, dt, index=330 + len(lengths) + d)
+        w = wl.make_workload(spec, device="cuda")
+        r = oracle_step(w)
+        g = gpu_step(w, partition_size=psize)
+        _report(f"reduce over {-(-max(lengths) // psize)} partitions {dt}", max_abs_err(g.out, r.out),
+                TOL[dt])
 
 
 def test_bf16_output():
