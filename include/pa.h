@@ -269,6 +269,49 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
                               int partition_size, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * pa_prefill -- multi-token queries over the paged cache (a prompt, or a
+ * chunk of one, whose K and V were already written with
+ * pa_reshape_and_cache).
+ *
+ * "Problem 1" on "vLLM Solved the Wrong Bottleneck" follows a prompt and then
+ * each generated token, every one of which needs the keys and values of all
+ * tokens before it; the paged cache keeps them in blocks reached through the
+ * block table ("The idea vLLM started from: pages" on "What vLLM Is and Why It
+ * Exists"). Reading (no formula on the pages): sequence s brings
+ * q_s = query_start[s + 1] - query_start[s] query rows, the last q_s tokens
+ * of its context of L = context_lens[s] tokens. Row i (query row
+ * query_start[s] + i) sits at position pos = L - q_s + i; for each query
+ * head h (KV head k = h / G):
+ *     out[row][h][:] = sum_{t <= pos} softmax_t(scale * q[row][h] . K_t) V_t
+ * with K_t, V_t read through the table as in pa_decode. q_s = 1 is a decode
+ * step; q_s = L is a whole prompt.
+ *
+ *   out              [T][Hq][D], T = query_start[S]; PA_F32 or PA_BF16.
+ *   query            [T][Hq][D], bf16 (the kv_dtype).
+ *   key_cache,
+ *   value_cache      [NB][Hkv][16][D], bf16 (PA_EUNSUPPORTED otherwise).
+ *   query_start      int32 [S + 1], device: 0 = query_start[0] <=
+ *                    query_start[1] <= ...; rows of sequence s are
+ *                    query_start[s] .. query_start[s + 1] - 1.
+ *   max_query_len    an upper bound on every q_s, known on the host; it sizes
+ *                    the grid. Of a longer q_s only the first max_query_len
+ *                    rows are computed (at their positions L - q_s + i); the
+ *                    rest are not written.
+ *   Other arguments, alignment and status codes as pa_decode; max_query_len
+ *   < 0 is PA_EINVAL; num_seqs = 0 or max_query_len = 0 enqueues nothing.
+ *   Device-side: a sequence with q_s > L, a context longer than its table
+ *   (L > 16 MB) or an empty pool gets NaN rows; a table id outside [0, NB)
+ *   within the context gives NaN rows for that sequence (no load leaves the
+ *   pool). Nothing is allocated; the call is asynchronous on `stream`.
+ */
+pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query,
+                       const void* key_cache, const void* value_cache, pa_dtype_t kv_dtype,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                       int num_q_heads, int num_kv_heads, int head_size, int block_size,
+                       int64_t num_blocks, float scale, int max_query_len, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* pa_status_str(pa_status_t status);
 

@@ -9,10 +9,12 @@ declared in ``include/pa.h``). This package is its thin Python binding:
     pa_decode_partitioned  split-context decode with a log-sum-exp reduce
     pa_decode_cascade      decode over a prefix that every sequence shares,
                            read once per KV head, plus per-sequence suffixes
+    pa_prefill             multi-token queries (a prompt or a chunk of one)
+                           attending causally over the paged cache
 """
 from ._lib import (  # noqa: F401
     PA_BF16, PA_F32, PagedAttentionError, cascade_workspace, decode_workspace, load,
     pa_copy_blocks, pa_decode, pa_decode_cascade, pa_decode_cascade_workspace_size,
-    pa_decode_partitioned, pa_decode_partitioned_workspace_size, pa_reshape_and_cache,
+    pa_decode_partitioned, pa_decode_partitioned_workspace_size, pa_prefill, pa_reshape_and_cache,
     pa_status_str, workspace_partials,
 )

@@ -19,7 +19,7 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, 1, 2, 3, 4
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_partitioned",
            "pa_decode_partitioned_workspace_size", "pa_decode_cascade",
-           "pa_decode_cascade_workspace_size", "pa_status_str")
+           "pa_decode_cascade_workspace_size", "pa_prefill", "pa_status_str")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -58,6 +58,9 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_cascade.restype = i32
     lib.pa_decode_cascade_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_cascade_workspace_size.restype = sz
+    lib.pa_prefill.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                               i64, f32, i32, vp]
+    lib.pa_prefill.restype = i32
     lib.pa_status_str.argtypes = [i32]
     lib.pa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -164,6 +167,36 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                           block_tables.data_ptr(), MB, context_lens.data_ptr(), S, Hq, Hkv, D, B,
                           NB, float(scale), _stream(query, stream))
     _check(rc, "pa_decode")
+    return out
+
+
+def pa_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+               value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+               query_start: torch.Tensor, scale: float, max_query_len: int,
+               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Multi-token queries over the paged cache. query and out are [T, Hq, D]; the rows of
+    sequence s are query_start[s] .. query_start[s + 1] - 1 (int32 [S + 1] on the GPU), the
+    last tokens of its context, each attending causally. max_query_len bounds every
+    sequence's row count. out (float32 or bfloat16) is written asynchronously and returned."""
+    _dev(out, query, key_cache, value_cache, block_tables, context_lens, query_start)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or \
+            query_start.dtype != torch.int32:
+        raise TypeError("block_tables, context_lens and query_start must be int32")
+    T, Hq, D = query.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    S = context_lens.shape[0]
+    if D2 != D or value_cache.shape != key_cache.shape or out.shape != query.shape:
+        raise ValueError("query/out/cache shapes disagree")
+    if query.dtype != key_cache.dtype or value_cache.dtype != key_cache.dtype:
+        raise TypeError("query and caches must share one dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.shape != (S + 1,):
+        raise ValueError("block_tables must be [S, MB] and query_start [S + 1]")
+    rc = load().pa_prefill(out.data_ptr(), _dtype_code(out.dtype), query.data_ptr(),
+                           key_cache.data_ptr(), value_cache.data_ptr(), _dtype_code(key_cache.dtype),
+                           block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+                           query_start.data_ptr(), S, Hq, Hkv, D, B, NB, float(scale),
+                           int(max_query_len), _stream(query, stream))
+    _check(rc, "pa_prefill")
     return out
 
 

@@ -429,4 +429,47 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
     return from_hip(pa::launch_reduce(r, head_size, out_dtype == PA_BF16, num_seqs, s));
 }
 
+pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query, const void* key_cache,
+                       const void* value_cache, pa_dtype_t kv_dtype, const int32_t* block_tables,
+                       int max_blocks_per_seq, const int32_t* context_lens,
+                       const int32_t* query_start, int num_seqs, int num_q_heads, int num_kv_heads,
+                       int head_size, int block_size, int64_t num_blocks, float scale,
+                       int max_query_len, void* stream) {
+    pa_status_t st = check_decode(out, out_dtype, query, key_cache, value_cache, kv_dtype,
+                                  block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                  scale);
+    if (st != PA_OK)
+        return st;
+    if (kv_dtype != PA_BF16)
+        return PA_EUNSUPPORTED;
+    if (max_query_len < 0)
+        return PA_EINVAL;
+    if (num_seqs == 0 || max_query_len == 0)
+        return PA_OK;
+    if (!query_start || !aligned(query_start, 4))
+        return PA_EINVAL;
+    const int64_t rows = static_cast<int64_t>(max_query_len) * (num_q_heads / num_kv_heads);
+    if (rows > INT32_MAX)
+        return PA_EUNSUPPORTED;
+    const int64_t tiles = (rows + pa::kPrefillWaves * 16 - 1) / (pa::kPrefillWaves * 16);
+    pa::PrefillParams p{};
+    p.q = query;
+    p.k_cache = key_cache;
+    p.v_cache = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.query_start = query_start;
+    p.out = out;
+    p.num_blocks = num_blocks;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_q_heads / num_kv_heads;
+    p.max_query_len = max_query_len;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return from_hip(pa::launch_prefill(p, head_size, out_dtype == PA_BF16, num_seqs,
+                                       static_cast<int>(tiles), static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -24,60 +24,16 @@
 //   * V is written to LDS transposed (token-contiguous rows, padded so that
 //     the B-operand reads are conflict-free) and P.V runs on MFMA with the
 //     output rows in the same lanes as the softmax state.
-#include "pa_internal.h"
+#include "pa_device.h"
 
 namespace pa {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+using namespace dev;
 
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kStepTokens = 32;                 // two blocks per step
 constexpr int kVtStride = kStepTokens + 8;      // bf16 per transposed V row (80 bytes)
 constexpr int kPStride = kStepTokens + 4;       // floats per P row in LDS (144 bytes)
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float row_max16(float x) {
-    x = fmaxf(x, dpp<0xB1>(x));
-    x = fmaxf(x, dpp<0x4E>(x));
-    x = fmaxf(x, dpp<0x141>(x));
-    x = fmaxf(x, dpp<0x140>(x));
-    return x;
-}
-
-__device__ __forceinline__ float row_sum16(float x) {
-    x = x + dpp<0xB1>(x);
-    x = x + dpp<0x4E>(x);
-    x = x + dpp<0x141>(x);
-    x = x + dpp<0x140>(x);
-    return x;
-}
-
-// fp32 -> bf16 bits, round to nearest even (P is finite and non-negative).
-__device__ __forceinline__ uint16_t bf16_bits(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-}
-
-__device__ __forceinline__ float bf16_value(uint16_t b) {
-    return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-
-// Workgroup barrier that orders LDS traffic only: global loads in flight
-// (the next step's K and V) stay in flight across it.
-__device__ __forceinline__ void wave_lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int D>
 __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(CascadeParams p) {
@@ -217,7 +173,7 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 o[n][j] *= alpha[j];
-        wave_lds_barrier();                     // P of every wave and all of V^T are in LDS
+        lds_barrier();                     // P of every wave and all of V^T are in LDS
         // P as the A operand (row r16, tokens 8g..8g+7), split into bf16 hi + lo.
         u16x8 phi, plo;
         {
@@ -239,7 +195,7 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
             o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo),
                                                            __builtin_bit_cast(bf16x8, vb), o[n], 0, 0, 0);
         }
-        wave_lds_barrier();                     // LDS free for the next step
+        lds_barrier();                     // LDS free for the next step
     }
 
     // Row partials of this chunk: rows 4g+j of the wave, columns n*16 + r16.

@@ -1,0 +1,68 @@
+// pa_device.h -- device helpers shared by the MFMA attention kernels over
+// dense query tiles (shared-prefix and multi-token-query kernels).
+#pragma once
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace dev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Max / sum over the 16 lanes of a DPP row (quad swaps, then half-row and
+// row mirrors); every lane of the row gets the result.
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    x = fmaxf(x, dpp<0x140>(x));
+    return x;
+}
+
+__device__ __forceinline__ float row_sum16(float x) {
+    x = x + dpp<0xB1>(x);
+    x = x + dpp<0x4E>(x);
+    x = x + dpp<0x141>(x);
+    x = x + dpp<0x140>(x);
+    return x;
+}
+
+// fp32 -> bf16 bits, round to nearest even (for finite values).
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_value(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even, NaN kept NaN (output rows).
+__device__ __forceinline__ uint16_t bf16_out(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return static_cast<uint16_t>((u >> 16) | 0x40u);
+    return bf16_bits(x);
+}
+
+// Workgroup barrier that orders LDS traffic only: global loads in flight stay
+// in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace dev
+}  // namespace pa

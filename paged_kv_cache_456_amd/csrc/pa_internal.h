@@ -14,6 +14,7 @@ constexpr int kPartWaves = 4;    // waves per decode workgroup (partitioned)
 constexpr int kReduceThreads = 256;
 constexpr int kCascadeWaves = 4;          // 64 query rows per prefix workgroup
 constexpr int kCascadeChunkBlocks = 16;   // prefix blocks per prefix workgroup
+constexpr int kPrefillWaves = 4;          // 64 query rows per multi-token-query workgroup
 
 // Element tags for the KV dtype.
 struct BF16 {
@@ -146,6 +147,24 @@ struct CascadeParams {
     float scale_log2;
 };
 
+// Multi-token queries over the paged cache (prompt / chunked prefill).
+struct PrefillParams {
+    const void* q;                 // [T][Hq][D] bf16, T = query_start[S]
+    const void* k_cache;           // [NB][Hkv][16][D] bf16
+    const void* v_cache;
+    const int32_t* block_tables;   // [S][MB]
+    const int32_t* context_lens;   // [S]
+    const int32_t* query_start;    // [S + 1]
+    void* out;                     // [T][Hq][D]
+    int64_t num_blocks;
+    int max_blocks_per_seq;
+    int num_q_heads;
+    int num_kv_heads;
+    int group;
+    int max_query_len;             // rows past this many per sequence are not computed
+    float scale_log2;              // scale * log2(e)
+};
+
 struct CopyParams {
     uint8_t* key_cache;
     uint8_t* value_cache;
@@ -163,5 +182,7 @@ hipError_t launch_cache(const CacheParams& p, int64_t num_tokens, hipStream_t st
 hipError_t launch_copy_blocks(const CopyParams& p, int64_t num_pairs, hipStream_t stream);
 hipError_t launch_cascade_prefix(const CascadeParams& p, int head_size, int num_chunks,
                                  hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int head_size, int out_bf16, int num_seqs,
+                          int row_tiles, hipStream_t stream);
 
 }  // namespace pa

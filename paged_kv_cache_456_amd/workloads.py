@@ -327,3 +327,19 @@ def exp_lengths(n: int, rng: np.random.Generator, base: int = 100, mean: float =
     """n draws of the skewed length law min(cap, base + floor(Exp(mean)))."""
     draws = np.floor(rng.exponential(mean, size=n)).astype(np.int64)
     return np.minimum(cap, base + draws)
+
+
+def prefill_queries(w: Workload, query_lens: List[int], seed: int = 0):
+    """Query rows for multi-token queries over workload w: sequence s brings the last
+    query_lens[s] tokens of its context (each <= its context length). Returns
+    (query [T, Hq, D] in the workload dtype, N(0, 1) values drawn on w's device,
+    query_start int32 [S + 1] as a numpy array, 0 first)."""
+    ql = np.asarray(query_lens, dtype=np.int64)
+    if len(ql) != w.num_seqs or (ql < 0).any():
+        raise ValueError("one non-negative query length per sequence")
+    qs = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    dev = w.key_cache.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(_VALUE_SEED_BASE + 500 + w.spec.index + 7919 * seed)
+    q = _normal((int(qs[-1]), w.query.shape[1], w.query.shape[2]), w.query.dtype, gen, dev)
+    return q, qs

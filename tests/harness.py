@@ -31,12 +31,10 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
-def oracle_step(w: Workload, seqs: Optional[Sequence[int]] = None,
-                partition_size: Optional[int] = None, num_threads: int = 0) -> OracleResult:
-    """Cache write + decode in the oracle for the given sequences (all by default), on a
-    host copy of just the blocks those sequences reach, taken before any GPU write."""
-    S = w.num_seqs
-    seqs = np.arange(S) if seqs is None else np.asarray(seqs)
+def oracle_cache(w: Workload, seqs: np.ndarray):
+    """Host copy of just the blocks the given sequences reach, taken before any GPU write,
+    with the oracle's own cache write of those sequences' new tokens applied. Returns
+    (original ids of the compacted blocks, tables remapped to them, key pool, value pool)."""
     B = w.block_size
     L = w.context_lens.astype(np.int64)
     nblk = -(-L // B)
@@ -61,6 +59,15 @@ def oracle_step(w: Workload, seqs: Optional[Sequence[int]] = None,
     kcn, vcn = _bits(kc).numpy(), _bits(vc).numpy()
     oracle.reshape_and_cache(_bits(key).numpy().copy(), _bits(value).numpy().copy(), kcn, vcn,
                              new_slots, block_size=B)
+    return blocks, tables, kc, vc
+
+
+def oracle_step(w: Workload, seqs: Optional[Sequence[int]] = None,
+                partition_size: Optional[int] = None, num_threads: int = 0) -> OracleResult:
+    """Cache write + decode in the oracle for the given sequences (all by default), on a
+    host copy of just the blocks those sequences reach, taken before any GPU write."""
+    seqs = np.arange(w.num_seqs) if seqs is None else np.asarray(seqs)
+    blocks, tables, kc, vc = oracle_cache(w, seqs)
     q = w.query[torch.from_numpy(seqs).to(w.query.device)].cpu()
     cl = w.context_lens[seqs]
     if partition_size is None:

@@ -189,3 +189,24 @@ def test_cascade_workspace_size_formula(lib):
             2 * a256(4 * R) + a256(4 * R * D)
     assert pa.pa_decode_cascade_workspace_size(4, 4, 64, 10, 16, 0) == 0
     assert pa.pa_decode_cascade_workspace_size(4, 4, 64, 10, 0, 1) == 0
+
+
+def prefill_call(lib, qs=P, max_q=8, **kw):
+    a = decode_args(kv_dt=1)
+    a.update(kw)
+    return lib.pa_prefill(a["out"], a["out_dt"], a["q"], a["kc"], a["vc"], a["kv_dt"], a["bt"],
+                          a["MB"], a["cl"], qs, a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
+                          a["scale"], max_q, None)
+
+
+@pytest.mark.parametrize("kw,expect", [c for c in DECODE_CASES if "kv_dt" not in c[0]])
+def test_prefill_shares_decode_checks(lib, kw, expect):
+    assert prefill_call(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(kv_dt=0), EUNSUP), (dict(max_q=-1), EINVAL), (dict(qs=0), EINVAL), (dict(qs=P + 2), EINVAL),
+    (dict(max_q=0, qs=0), OK), (dict(S=0, qs=0), OK), (dict(max_q=1 << 30, Hq=16, Hkv=2), EUNSUP),
+])
+def test_prefill_checks(lib, kw, expect):
+    assert prefill_call(lib, **kw) == expect
