@@ -71,8 +71,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
-                    help="decode: the decode step (default); copy_blocks: pa_copy_blocks alone")
+    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill"), default="decode",
+                    help="decode: the decode step (default); copy_blocks: pa_copy_blocks alone; "
+                         "prefill: pa_prefill, a chunk of query tokens per sequence")
+    ap.add_argument("--prefill-chunk", type=int, default=512,
+                    help="--op prefill: query tokens per sequence (its last min(L, chunk) tokens)")
     ap.add_argument("--workload", default="llama8b_gqa_bf16")
     ap.add_argument("--kernel", choices=("partitioned", "single", "cascade"), default="partitioned",
                     help="cascade: pa_decode_cascade over the prefix every table shares "
@@ -105,6 +108,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.op == "copy_blocks":
         return bench_copy_blocks(args, dev)
+    if args.op == "prefill":
+        return bench_prefill(args, dev)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -307,6 +312,75 @@ def bench_copy_blocks(args, dev) -> int:
                      "kernel": "copy_blocks_kernel",
                      "timing": "HIP events around the timed calls, mean per call"},
         "cow_128_pairs_us": round(small_s * 1e6, 3),
+        "cpu_baseline": None,
+    }), flush=True)
+    return 0
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(args, dev) -> int:
+    """pa_prefill on the Llama-8B-shaped batch (64 sequences, 32/8 heads, D = 128, bf16,
+    the headline context lengths): each sequence brings its last min(L, chunk) tokens as
+    query rows (a chunked-prefill step), attending causally over its paged context.
+    Algorithmic work = 4 D Hq sum over rows of (position + 1) flops (Q K^T and P V, causal);
+    the bound is bf16 MFMA. Synthetic data, inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_456_amd as pa
+    from paged_kv_cache_456_amd import workloads as wl
+
+    w = wl.make_workload(args.workload, device=dev)
+    S, Hq, D = w.query.shape
+    if w.query.dtype != torch.bfloat16:
+        print("--op prefill needs a bf16 workload", file=sys.stderr)
+        return 2
+    L = w.context_lens.astype(np.int64)
+    ql = np.minimum(L, args.prefill_chunk)
+    q, qs = wl.prefill_queries(w, ql.tolist())
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    cl = torch.from_numpy(w.context_lens).to(dev)
+    pa.pa_reshape_and_cache(w.key, w.value, w.key_cache, w.value_cache,
+                            torch.from_numpy(w.slot_mapping).to(dev))
+    qs_d = torch.from_numpy(qs).to(dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    mq = int(ql.max())
+    visible = int((ql * (L - ql) + ql * (ql + 1) // 2).sum())     # sum over rows of pos + 1
+    flops = 4 * D * Hq * visible
+
+    def call():
+        pa.pa_prefill(out, q, w.key_cache, w.value_cache, bt, cl, qs_d, w.scale, mq)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    dev_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    tflops = flops / dev_s / 1e12
+    log(f"[bench] prefill: {int(ql.sum())} query tokens over {S} sequences, {flops / 1e9:.2f} GFLOP "
+        f"per call, {dev_s * 1e6:.1f} us per call")
+    print(json.dumps({
+        "metric": "multi-token query attention TFLOP/s (causal, algorithmic)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload} prefill chunk {args.prefill_chunk}",
+                   "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": int(w.key_cache.shape[1]),
+                   "head_size": D, "query_tokens": int(ql.sum()), "sum_context_len": int(L.sum()),
+                   "flops_per_call": flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_kernel",
+                     "timing": "HIP events around the timed calls, mean per call"},
         "cpu_baseline": None,
     }), flush=True)
     return 0
