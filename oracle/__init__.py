@@ -1,5 +1,6 @@
 """fp64 CPU oracle for paged decode attention, multi-token queries over the paged
-cache, the KV-cache write and the copy-on-write block copy.
+cache, the KV-cache write and the copy-on-write block copy (the block manager's
+reference model is the plain Python of ``block_manager.py``).
 
 TEST INFRASTRUCTURE ONLY. The test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` are the only callers. The GPU library never
