@@ -59,6 +59,7 @@
  *                                 an unsupported dtype
  *                PA_EWORKSPACE    workspace smaller than required
  *                PA_EHIP          the kernel launch failed
+ *                PA_ENOSPACE      (block manager) no free block for the request
  *              Device-resident inputs are not copied to the host. The kernels
  *              check them anyway and never touch memory outside the pools:
  *              a sequence whose context is longer than its table (or than
@@ -83,7 +84,8 @@ typedef enum {
     PA_EINVAL = 1,
     PA_EUNSUPPORTED = 2,
     PA_EWORKSPACE = 3,
-    PA_EHIP = 4
+    PA_EHIP = 4,
+    PA_ENOSPACE = 5
 } pa_status_t;
 
 /*
@@ -311,6 +313,73 @@ pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query,
                        const int32_t* context_lens, const int32_t* query_start, int num_seqs,
                        int num_q_heads, int num_kv_heads, int head_size, int block_size,
                        int64_t num_blocks, float scale, int max_query_len, void* stream);
+
+/*
+ * Block manager -- host-side owner of the pool's blocks and of every
+ * sequence's block table (the producer of the block_tables, slot_mapping and
+ * copy-on-write block_mapping arguments above).
+ *
+ * "Idea 1: PagedAttention" on the day-9 post: the cache is split into
+ * fixed-size blocks, a block table maps a request's logical blocks to
+ * physical ones, requests with a common prefix share physical blocks, and a
+ * shared block that must diverge is copied alone ("Why this wins"). "The idea
+ * vLLM started from: pages" on "What vLLM Is and Why It Exists": blocks are
+ * handed out on demand; "preemption" takes a request's blocks away to feed
+ * another. Readings where the pages are silent:
+ *   - free blocks form a stack, initially with block 0 on top (a fresh pool
+ *     hands out 0, 1, 2, ...); a released block goes on top;
+ *   - releasing a table walks it from its first entry to its last; a block is
+ *     free again when no table holds it;
+ *   - adding a sequence takes all of its blocks or none (PA_ENOSPACE);
+ *   - appending the token at position L takes a new block when L is a
+ *     multiple of block_size; otherwise, if the last block is shared, it is
+ *     replaced by a fresh block and (old, new) is reported: the caller copies
+ *     block old onto block new (pa_copy_blocks) before writing the token;
+ *   - slot of position t = table[t / block_size] * block_size + t % block_size.
+ * Preempting a sequence is pa_bm_free_sequence; choosing the victim is the
+ * caller's. Host memory only (no GPU call). One manager must not be used from
+ * two threads at once; different managers are independent.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager of num_blocks (0 .. INT32_MAX) blocks of block_size tokens; NULL
+ * for bad arguments or when host memory runs out. */
+pa_block_manager* pa_bm_create(int64_t num_blocks, int block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* A new sequence seq_id of num_tokens >= 0 tokens: ceil(num_tokens /
+ * block_size) blocks, and slots_out[t] (host array of num_tokens) = the slot
+ * of token t. PA_EINVAL for an id in use or a negative count; PA_ENOSPACE
+ * (nothing changed) when too few blocks are free. */
+pa_status_t pa_bm_add_sequence(pa_block_manager* bm, int64_t seq_id, int num_tokens,
+                               int64_t* slots_out);
+
+/* Room for one more token of seq_id: *slot_out = its slot; cow_out[0..1] =
+ * (source, destination) block of a copy-on-write the caller must perform
+ * first, or (-1, -1). PA_EINVAL for an unknown id; PA_ENOSPACE (nothing
+ * changed) when a block is needed and none is free. */
+pa_status_t pa_bm_append_token(pa_block_manager* bm, int64_t seq_id, int64_t* slot_out,
+                               int64_t* cow_out);
+
+/* child_id (a new id) gets parent_id's table and length; every block of it is
+ * now shared. PA_EINVAL for an unknown parent or an id in use. */
+pa_status_t pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id);
+
+/* Releases seq_id's table (also how a sequence is preempted). PA_EINVAL for an
+ * unknown id. */
+pa_status_t pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id);
+
+/* Free blocks (-1 for a NULL manager). */
+int64_t pa_bm_num_free_blocks(const pa_block_manager* bm);
+
+/* Tokens held by seq_id, or -1 for an unknown id. */
+int64_t pa_bm_length(const pa_block_manager* bm, int64_t seq_id);
+
+/* Writes seq_id's block table to table_out[0 .. max_entries) (host), padding
+ * past its end with `pad`; returns its number of blocks (which may exceed
+ * max_entries), or -1 for an unknown id or bad arguments. */
+int64_t pa_bm_block_table(const pa_block_manager* bm, int64_t seq_id, int32_t* table_out,
+                          int max_entries, int32_t pad);
 
 /* A static, human-readable name for a status code. */
 const char* pa_status_str(pa_status_t status);

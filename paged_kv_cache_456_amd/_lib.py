@@ -15,11 +15,14 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32, PA_BF16 = 0, 1
-PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, 1, 2, 3, 4
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOSPACE = 0, 1, 2, 3, 4, 5
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_partitioned",
            "pa_decode_partitioned_workspace_size", "pa_decode_cascade",
-           "pa_decode_cascade_workspace_size", "pa_prefill", "pa_status_str")
+           "pa_decode_cascade_workspace_size", "pa_prefill", "pa_status_str",
+           "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token",
+           "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_num_free_blocks", "pa_bm_length",
+           "pa_bm_block_table")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -61,6 +64,24 @@ def load() -> ctypes.CDLL:
     lib.pa_prefill.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                i64, f32, i32, vp]
     lib.pa_prefill.restype = i32
+    lib.pa_bm_create.argtypes = [i64, i32]
+    lib.pa_bm_create.restype = vp
+    lib.pa_bm_destroy.argtypes = [vp]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_add_sequence.argtypes = [vp, i64, i32, vp]
+    lib.pa_bm_add_sequence.restype = i32
+    lib.pa_bm_append_token.argtypes = [vp, i64, vp, vp]
+    lib.pa_bm_append_token.restype = i32
+    lib.pa_bm_fork.argtypes = [vp, i64, i64]
+    lib.pa_bm_fork.restype = i32
+    lib.pa_bm_free_sequence.argtypes = [vp, i64]
+    lib.pa_bm_free_sequence.restype = i32
+    lib.pa_bm_num_free_blocks.argtypes = [vp]
+    lib.pa_bm_num_free_blocks.restype = i64
+    lib.pa_bm_length.argtypes = [vp, i64]
+    lib.pa_bm_length.restype = i64
+    lib.pa_bm_block_table.argtypes = [vp, i64, vp, i32, ctypes.c_int32]
+    lib.pa_bm_block_table.restype = i64
     lib.pa_status_str.argtypes = [i32]
     lib.pa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -292,3 +313,77 @@ def workspace_partials(workspace: torch.Tensor, num_seqs: int, num_q_heads: int,
     po = flat[2 * o1:2 * o1 + rows * 4 * head_size].view(torch.float32).view(
         num_seqs, num_q_heads, np_, head_size)
     return pm, ps, po
+
+
+class NoSpace(PagedAttentionError):
+    """The block manager has no free block for the request (nothing changed)."""
+
+
+class BlockManager:
+    """The library's host-side block manager (pa_bm_* in include/pa.h): blocks of the
+    pool handed out on demand, per-sequence block tables, shared blocks with reference
+    counts, copy-on-write pairs on appends to a shared block."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        self._lib = load()
+        self._h = self._lib.pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise PagedAttentionError(PA_EINVAL, "pa_bm_create")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _check(self, rc: int, where: str) -> None:
+        if rc == PA_ENOSPACE:
+            raise NoSpace(rc, where)
+        if rc != PA_OK:
+            raise PagedAttentionError(rc, where)
+
+    def add_sequence(self, seq: int, num_tokens: int):
+        """Blocks for a new sequence; returns the slots of its tokens (list of int)."""
+        out = (ctypes.c_int64 * max(1, int(num_tokens)))()
+        self._check(self._lib.pa_bm_add_sequence(self._h, int(seq), int(num_tokens), out),
+                    "pa_bm_add_sequence")
+        return list(out[:int(num_tokens)])
+
+    def append_token(self, seq: int):
+        """Room for one more token: (slot, (src, dst) copy-on-write pair or None)."""
+        slot = ctypes.c_int64()
+        cow = (ctypes.c_int64 * 2)()
+        self._check(self._lib.pa_bm_append_token(self._h, int(seq), ctypes.byref(slot), cow),
+                    "pa_bm_append_token")
+        return slot.value, (None if cow[0] < 0 else (cow[0], cow[1]))
+
+    def fork(self, parent: int, child: int) -> None:
+        self._check(self._lib.pa_bm_fork(self._h, int(parent), int(child)), "pa_bm_fork")
+
+    def free_sequence(self, seq: int) -> None:
+        self._check(self._lib.pa_bm_free_sequence(self._h, int(seq)), "pa_bm_free_sequence")
+
+    preempt = free_sequence
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free_blocks(self._h))
+
+    def length(self, seq: int) -> int:
+        n = int(self._lib.pa_bm_length(self._h, int(seq)))
+        if n < 0:
+            raise PagedAttentionError(PA_EINVAL, "pa_bm_length")
+        return n
+
+    def table(self, seq: int, width: int = 0, pad: int = -1):
+        """The sequence's block table (list), padded with `pad` to `width` entries if wider."""
+        n = int(self._lib.pa_bm_block_table(self._h, int(seq), None, 0, 0))
+        if n < 0:
+            raise PagedAttentionError(PA_EINVAL, "pa_bm_block_table")
+        w = max(n, int(width))
+        buf = (ctypes.c_int32 * max(1, w))()
+        self._lib.pa_bm_block_table(self._h, int(seq), buf, w, int(pad))
+        return list(buf[:w])

@@ -111,6 +111,7 @@ const char* pa_status_str(pa_status_t status) {
     case PA_EUNSUPPORTED: return "unsupported configuration";
     case PA_EWORKSPACE: return "workspace too small";
     case PA_EHIP: return "HIP launch failed";
+    case PA_ENOSPACE: return "no free block";
     }
     return "unknown status";
 }
