@@ -1,0 +1,137 @@
+"""The block manager driving the kernels through continuous-batching steps on the GPU.
+
+Each step: requests arrive (prompt tokens written with pa_reshape_and_cache), some fork
+(sharing their blocks), some finish; then every running sequence appends one token. The
+library's block manager hands out the slots; a copy-on-write pair it reports is applied
+with pa_copy_blocks right away; when the pool is full the youngest sequence that has not
+stepped yet is preempted. The step's decode (pa_decode_partitioned and pa_decode over the
+manager's tables) is compared with the fp64 oracle run on caches rebuilt from each
+sequence's own token history -- never from the GPU pool -- so a wrong slot, a missed or
+misdirected copy, or a stale table shows up as an error."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_456_amd as pa
+from harness import TOL
+
+pytestmark = pytest.mark.gpu
+
+B, HQ, HKV, D = 16, 8, 2, 64
+NB, MB = 48, 16
+MAX_ORIGINS, MAX_POS = 160, MB * B
+
+
+def test_continuous_batching_steps():
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(4242)
+    # K/V of token `pos` of the sequence that first produced it (its origin).
+    kv_k = torch.randn((MAX_ORIGINS, MAX_POS, HKV, D), generator=gen).to(torch.bfloat16)
+    kv_v = torch.randn((MAX_ORIGINS, MAX_POS, HKV, D), generator=gen).to(torch.bfloat16)
+    kc = torch.full((NB, HKV, B, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = torch.full_like(kc, float("nan"))
+    scale = D ** -0.5
+    bm = pa.BlockManager(NB, B)
+    rng = np.random.default_rng(9)
+    hist = {}                  # sequence -> list of token tags (origin, position)
+    order = []                 # running sequences, oldest first
+    next_id = 0
+    stats = {"cow": 0, "preempt": 0, "fork": 0, "checked": 0}
+
+    def write(tags, slots):
+        o = torch.tensor([t[0] for t in tags])
+        p = torch.tensor([t[1] for t in tags])
+        pa.pa_reshape_and_cache(kv_k[o, p].to(dev), kv_v[o, p].to(dev), kc, vc,
+                                torch.tensor(slots, dtype=torch.int64, device=dev))
+
+    for step in range(40):
+        # arrivals
+        for _ in range(int(rng.integers(0, 3)) if order else 2):
+            if next_id >= MAX_ORIGINS:
+                break
+            n = int(rng.integers(1, 40))
+            try:
+                slots = bm.add_sequence(next_id, n)
+            except pa.NoSpace:
+                break
+            hist[next_id] = [(next_id, t) for t in range(n)]
+            write(hist[next_id], slots)
+            order.append(next_id)
+            next_id += 1
+        # a fork shares the parent's blocks; a finish releases a sequence's blocks
+        if order and rng.random() < 0.3 and next_id < MAX_ORIGINS:
+            parent = order[int(rng.integers(0, len(order)))]
+            bm.fork(parent, next_id)
+            hist[next_id] = list(hist[parent])
+            order.append(next_id)
+            next_id += 1
+            stats["fork"] += 1
+        if len(order) > 2 and rng.random() < 0.3:
+            s = order.pop(int(rng.integers(0, len(order))))
+            bm.free_sequence(s)
+            del hist[s]
+        # the decode step: one new token per running sequence
+        stepped, tags, slots = [], [], []
+        for s in list(order):
+            if s not in hist or len(hist[s]) >= MAX_POS:
+                continue
+            while True:
+                try:
+                    slot, cow = bm.append_token(s)
+                    break
+                except pa.NoSpace:
+                    waiting = [v for v in order if v != s and v not in stepped]
+                    victim = waiting[-1] if waiting else s
+                    bm.preempt(victim)
+                    order.remove(victim)
+                    del hist[victim]
+                    stats["preempt"] += 1
+                    if victim == s:
+                        slot = None
+                        break
+            if slot is None:
+                continue
+            if cow is not None:
+                pa.pa_copy_blocks(kc, vc, torch.tensor([cow], dtype=torch.int64, device=dev))
+                stats["cow"] += 1
+            tag = (s, len(hist[s]))              # a new token is its own sequence's
+            hist[s].append(tag)
+            tags.append(tag)
+            slots.append(slot)
+            stepped.append(s)
+        if not stepped:
+            continue
+        write(tags, slots)
+        S = len(stepped)
+        q = torch.randn((S, HQ, D), generator=gen).to(torch.bfloat16)
+        bt = torch.tensor([bm.table(s, MB, pad=-1) for s in stepped], dtype=torch.int32, device=dev)
+        lens = [bm.length(s) for s in stepped]
+        assert lens == [len(hist[s]) for s in stepped]
+        cl = torch.tensor(lens, dtype=torch.int32, device=dev)
+        out = torch.empty((S, HQ, D), dtype=torch.float32, device=dev)
+        ws = pa.decode_workspace(S, HQ, D, MAX_POS, 32, device=dev)
+        pa.pa_decode_partitioned(out, q.to(dev), kc, vc, bt, cl, scale, MAX_POS, 32, ws)
+        out1 = torch.empty_like(out)
+        pa.pa_decode(out1, q.to(dev), kc, vc, bt, cl, scale)
+        torch.cuda.synchronize()
+        # oracle: each sequence's cache laid out contiguously from its own token history
+        nbs = [-(-n // B) for n in lens]
+        first = np.concatenate([[0], np.cumsum(nbs)])
+        kr = torch.zeros((int(first[-1]), HKV, B, D), dtype=torch.bfloat16)
+        vr = torch.zeros_like(kr)
+        tab = np.full((S, MB), -1, np.int32)
+        for i, s in enumerate(stepped):
+            o = torch.tensor([t[0] for t in hist[s]])
+            p = torch.tensor([t[1] for t in hist[s]])
+            for t in range(lens[i]):
+                kr[first[i] + t // B, :, t % B] = kv_k[o[t], p[t]]
+                vr[first[i] + t // B, :, t % B] = kv_v[o[t], p[t]]
+            tab[i, :nbs[i]] = np.arange(first[i], first[i] + nbs[i])
+        ref = oracle.decode(q, kr, vr, tab, np.array(lens, np.int32), scale)
+        for name, got in (("partitioned", out), ("single", out1)):
+            err = float(np.max(np.abs(got.double().cpu().numpy() - ref)))
+            assert err <= TOL[torch.bfloat16], f"step {step} {name}: {err}"
+        stats["checked"] += 1
+    print(stats, flush=True)
+    assert stats["cow"] > 0 and stats["preempt"] > 0 and stats["fork"] > 0 and stats["checked"] >= 30
