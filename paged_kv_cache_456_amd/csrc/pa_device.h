@@ -56,6 +56,25 @@ __device__ __forceinline__ uint16_t bf16_out(float x) {
     return bf16_bits(x);
 }
 
+// Splits eight finite fp32 values into a bf16 high part and the bf16 rounding
+// of the remainder (value - high), both round-to-nearest-even, with the
+// hardware's packed conversion: together they keep about 16 bits.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_bf16x8(const float (&v)[8], u16x8& hi, u16x8& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const bf16x2 h = {static_cast<__bf16>(v[i]), static_cast<__bf16>(v[i + 1])};
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const float h0 = __uint_as_float(hb << 16), h1 = __uint_as_float(hb & 0xFFFF0000u);
+        const bf16x2 l = {static_cast<__bf16>(v[i] - h0), static_cast<__bf16>(v[i + 1] - h1)};
+        const uint32_t lb = __builtin_bit_cast(uint32_t, l);
+        hi[i] = static_cast<uint16_t>(hb);
+        hi[i + 1] = static_cast<uint16_t>(hb >> 16);
+        lo[i] = static_cast<uint16_t>(lb);
+        lo[i + 1] = static_cast<uint16_t>(lb >> 16);
+    }
+}
+
 // Workgroup barrier that orders LDS traffic only: global loads in flight stay
 // in flight across it.
 __device__ __forceinline__ void lds_barrier() {

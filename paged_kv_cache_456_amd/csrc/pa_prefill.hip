@@ -245,12 +245,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(PrefillP
             const f32x4 a0 = *reinterpret_cast<const f32x4*>(&pl[wave][r16][8 * g]);
             const f32x4 a1 = *reinterpret_cast<const f32x4*>(&pl[wave][r16][8 * g + 4]);
             const float pv[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint16_t h = bf16_bits(pv[i]);
-                phi[i] = h;
-                plo[i] = bf16_bits(pv[i] - bf16_value(h));
-            }
+            split_bf16x8(pv, phi, plo);
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
