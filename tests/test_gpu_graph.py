@@ -1,0 +1,56 @@
+"""The library's calls captured in a HIP graph: every replay must equal the eager result
+bit for bit, with the program's own eager work and synchronisations between replays
+(nothing in the captured calls may depend on state a replay leaves behind)."""
+import pytest
+import torch
+
+import paged_kv_cache_456_amd as pa
+from paged_kv_cache_456_amd import workloads as wl
+from harness import device_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("kernel", ["partitioned", "single", "prefill"])
+def test_graph_replays_match_eager(kernel):
+    spec = wl.custom_spec([3000, 17, 700, 1, 256], 32, 8, 128, torch.bfloat16, index=350)
+    w = wl.make_workload(spec, device="cuda")
+    bt, cl, slots = device_inputs(w)
+    S, Hq, D = w.query.shape
+    mcl, P = int(w.max_context_len), 256
+    ws = pa.decode_workspace(S, Hq, D, mcl, P)
+    q = w.query
+    if kernel == "prefill":
+        q, qs = wl.prefill_queries(w, [min(int(n), 40) for n in w.context_lens])
+        qs = torch.from_numpy(qs).cuda()
+    out = torch.empty((q.shape[0], Hq, D), dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.pa_reshape_and_cache(w.key, w.value, w.key_cache, w.value_cache, slots)
+        if kernel == "partitioned":
+            pa.pa_decode_partitioned(out, q, w.key_cache, w.value_cache, bt, cl, w.scale, mcl, P, ws)
+        elif kernel == "single":
+            pa.pa_decode(out, q, w.key_cache, w.value_cache, bt, cl, w.scale)
+        else:
+            pa.pa_prefill(out, q, w.key_cache, w.value_cache, bt, cl, qs, w.scale, 40)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = torch.empty((S, Hq, D), dtype=torch.float32, device="cuda")
+    for r in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {r} differs"
+        # eager work between replays
+        pa.pa_decode(other, w.query, w.key_cache, w.value_cache, bt, cl, w.scale)
+        torch.cuda.synchronize()
