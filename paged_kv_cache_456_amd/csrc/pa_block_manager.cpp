@@ -81,18 +81,20 @@ pa_status_t pa_bm_add_sequence(pa_block_manager* bm, int64_t seq_id, int num_tok
     const int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
     if (need > static_cast<int64_t>(bm->free_stack.size()))
         return PA_ENOSPACE;
-    try {
-        pa_block_manager::Seq s;
-        s.table.reserve(static_cast<size_t>(need));
-        for (int64_t i = 0; i < need; ++i)
-            s.table.push_back(bm->take());
-        s.len = num_tokens;
-        for (int64_t t = 0; t < num_tokens; ++t)
-            slots_out[t] = bm->slot(s, t);
-        bm->seqs.emplace(seq_id, std::move(s));
+    pa_block_manager::Seq* s = nullptr;
+    try {                                       // allocations first: nothing changes on failure
+        auto ins = bm->seqs.emplace(seq_id, pa_block_manager::Seq());
+        s = &ins.first->second;
+        s->table.reserve(static_cast<size_t>(need));
     } catch (...) {
+        bm->seqs.erase(seq_id);
         return PA_EINVAL;
     }
+    for (int64_t i = 0; i < need; ++i)
+        s->table.push_back(bm->take());
+    s->len = num_tokens;
+    for (int64_t t = 0; t < num_tokens; ++t)
+        slots_out[t] = bm->slot(*s, t);
     return PA_OK;
 }
 
@@ -110,10 +112,11 @@ pa_status_t pa_bm_append_token(pa_block_manager* bm, int64_t seq_id, int64_t* sl
         if (bm->free_stack.empty())
             return PA_ENOSPACE;
         try {
-            s.table.push_back(bm->take());
+            s.table.reserve(s.table.size() + 1);   // may throw: before any block is taken
         } catch (...) {
             return PA_EINVAL;
         }
+        s.table.push_back(bm->take());
     } else {
         const int32_t last = s.table.back();
         if (bm->refs[last] > 1) {
@@ -138,10 +141,10 @@ pa_status_t pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id
     if (it == bm->seqs.end())
         return PA_EINVAL;
     try {
-        pa_block_manager::Seq child = it->second;
-        for (int32_t b : child.table)
+        pa_block_manager::Seq child = it->second;   // copies first: nothing changes on failure
+        auto ins = bm->seqs.emplace(child_id, std::move(child));
+        for (int32_t b : ins.first->second.table)
             bm->refs[b] += 1;
-        bm->seqs.emplace(child_id, std::move(child));
     } catch (...) {
         return PA_EINVAL;
     }
