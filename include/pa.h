@@ -294,14 +294,18 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
  *   key_cache,
  *   value_cache      [NB][Hkv][16][D], bf16 (PA_EUNSUPPORTED otherwise).
  *   query_start      int32 [S + 1], device: 0 = query_start[0] <=
- *                    query_start[1] <= ...; rows of sequence s are
+ *                    query_start[1] <= ... <= T; rows of sequence s are
  *                    query_start[s] .. query_start[s + 1] - 1.
+ *   num_query_rows   T, the rows of query and out (>= 0; 0 enqueues nothing).
+ *                    A sequence whose rows do not lie inside [0, T) is
+ *                    skipped (nothing read or written for it).
  *   max_query_len    an upper bound on every q_s, known on the host; it sizes
  *                    the grid. Of a longer q_s only the first max_query_len
  *                    rows are computed (at their positions L - q_s + i); the
  *                    rest are not written.
  *   Other arguments, alignment and status codes as pa_decode; max_query_len
- *   < 0 is PA_EINVAL; num_seqs = 0 or max_query_len = 0 enqueues nothing.
+ *   < 0 or num_query_rows < 0 is PA_EINVAL; num_seqs = 0, max_query_len = 0
+ *   or num_query_rows = 0 enqueues nothing.
  *   Device-side: a sequence with q_s > L, a context longer than its table
  *   (L > 16 MB) or an empty pool gets NaN rows; a table id outside [0, NB)
  *   within the context gives NaN rows for that sequence (no load leaves the
@@ -310,9 +314,10 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
 pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query,
                        const void* key_cache, const void* value_cache, pa_dtype_t kv_dtype,
                        const int32_t* block_tables, int max_blocks_per_seq,
-                       const int32_t* context_lens, const int32_t* query_start, int num_seqs,
-                       int num_q_heads, int num_kv_heads, int head_size, int block_size,
-                       int64_t num_blocks, float scale, int max_query_len, void* stream);
+                       const int32_t* context_lens, const int32_t* query_start,
+                       int64_t num_query_rows, int num_seqs, int num_q_heads, int num_kv_heads,
+                       int head_size, int block_size, int64_t num_blocks, float scale,
+                       int max_query_len, void* stream);
 
 /*
  * Block manager -- host-side owner of the pool's blocks and of every

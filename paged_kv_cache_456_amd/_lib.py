@@ -61,8 +61,8 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_cascade.restype = i32
     lib.pa_decode_cascade_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_cascade_workspace_size.restype = sz
-    lib.pa_prefill.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32,
-                               i64, f32, i32, vp]
+    lib.pa_prefill.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, i64, i32, i32, i32, i32,
+                               i32, i64, f32, i32, vp]
     lib.pa_prefill.restype = i32
     lib.pa_bm_create.argtypes = [i64, i32]
     lib.pa_bm_create.restype = vp
@@ -215,7 +215,7 @@ def pa_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
     rc = load().pa_prefill(out.data_ptr(), _dtype_code(out.dtype), query.data_ptr(),
                            key_cache.data_ptr(), value_cache.data_ptr(), _dtype_code(key_cache.dtype),
                            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
-                           query_start.data_ptr(), S, Hq, Hkv, D, B, NB, float(scale),
+                           query_start.data_ptr(), T, S, Hq, Hkv, D, B, NB, float(scale),
                            int(max_query_len), _stream(query, stream))
     _check(rc, "pa_prefill")
     return out

@@ -433,9 +433,9 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
 pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query, const void* key_cache,
                        const void* value_cache, pa_dtype_t kv_dtype, const int32_t* block_tables,
                        int max_blocks_per_seq, const int32_t* context_lens,
-                       const int32_t* query_start, int num_seqs, int num_q_heads, int num_kv_heads,
-                       int head_size, int block_size, int64_t num_blocks, float scale,
-                       int max_query_len, void* stream) {
+                       const int32_t* query_start, int64_t num_query_rows, int num_seqs,
+                       int num_q_heads, int num_kv_heads, int head_size, int block_size,
+                       int64_t num_blocks, float scale, int max_query_len, void* stream) {
     pa_status_t st = check_decode(out, out_dtype, query, key_cache, value_cache, kv_dtype,
                                   block_tables, max_blocks_per_seq, context_lens, num_seqs,
                                   num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
@@ -444,9 +444,9 @@ pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query, const
         return st;
     if (kv_dtype != PA_BF16)
         return PA_EUNSUPPORTED;
-    if (max_query_len < 0)
+    if (max_query_len < 0 || num_query_rows < 0)
         return PA_EINVAL;
-    if (num_seqs == 0 || max_query_len == 0)
+    if (num_seqs == 0 || max_query_len == 0 || num_query_rows == 0)
         return PA_OK;
     if (!query_start || !aligned(query_start, 4))
         return PA_EINVAL;
@@ -461,6 +461,7 @@ pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query, const
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.query_start = query_start;
+    p.num_query_rows = num_query_rows;
     p.out = out;
     p.num_blocks = num_blocks;
     p.max_blocks_per_seq = max_blocks_per_seq;

@@ -155,6 +155,7 @@ struct PrefillParams {
     const int32_t* block_tables;   // [S][MB]
     const int32_t* context_lens;   // [S]
     const int32_t* query_start;    // [S + 1]
+    int64_t num_query_rows;        // T: rows of q and out
     void* out;                     // [T][Hq][D]
     int64_t num_blocks;
     int max_blocks_per_seq;

@@ -75,7 +75,12 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(PrefillP
     const int s = blockIdx.z;
     const int G = p.group, Hq = p.num_q_heads, Hkv = p.num_kv_heads;
     const int q0 = p.query_start[s];
-    const int nq = p.query_start[s + 1] - q0;
+    const int64_t q_end = p.query_start[s + 1];
+    // Rows outside [0, T) are never touched: such a sequence is skipped whole.
+    // A decreasing pair of offsets brings no rows.
+    if (q0 < 0 || q_end > p.num_query_rows)
+        return;
+    const int nq = q_end > q0 ? static_cast<int>(q_end - q0) : 0;
     // Rows computed: the first min(nq, max_query_len) query tokens, every head
     // of the group (none when the sequence brings no rows).
     const int rows = min(nq, p.max_query_len) * G;

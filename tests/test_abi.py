@@ -191,11 +191,11 @@ def test_cascade_workspace_size_formula(lib):
     assert pa.pa_decode_cascade_workspace_size(4, 4, 64, 10, 0, 1) == 0
 
 
-def prefill_call(lib, qs=P, max_q=8, **kw):
+def prefill_call(lib, qs=P, max_q=8, T=32, **kw):
     a = decode_args(kv_dt=1)
     a.update(kw)
     return lib.pa_prefill(a["out"], a["out_dt"], a["q"], a["kc"], a["vc"], a["kv_dt"], a["bt"],
-                          a["MB"], a["cl"], qs, a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
+                          a["MB"], a["cl"], qs, T, a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
                           a["scale"], max_q, None)
 
 
@@ -207,6 +207,7 @@ def test_prefill_shares_decode_checks(lib, kw, expect):
 @pytest.mark.parametrize("kw,expect", [
     (dict(kv_dt=0), EUNSUP), (dict(max_q=-1), EINVAL), (dict(qs=0), EINVAL), (dict(qs=P + 2), EINVAL),
     (dict(max_q=0, qs=0), OK), (dict(S=0, qs=0), OK), (dict(max_q=1 << 30, Hq=16, Hkv=2), EUNSUP),
+    (dict(T=-1), EINVAL), (dict(T=0, qs=0), OK),
 ])
 def test_prefill_checks(lib, kw, expect):
     assert prefill_call(lib, **kw) == expect

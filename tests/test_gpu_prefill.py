@@ -119,6 +119,20 @@ def test_prefill_error_rows():
     out3, _, qs = run_pair(w, [40, 10, 5, 3], max_query_len=8)
     assert torch.isnan(out3[qs[0] + 8:qs[1]]).all()
     assert not torch.isnan(out3[qs[0]:qs[0] + 8]).any()
+    # Offsets outside the T query rows (sequence 0 starts before them, the last sequence
+    # ends beyond them): those sequences are skipped, nothing is read or written for them.
+    q, qs = wl.prefill_queries(w, [10, 10, 5, 3])
+    _, _, slots = device_inputs(w)
+    kcg, vcg = w.key_cache.clone(), w.value_cache.clone()
+    pa.pa_reshape_and_cache(w.key, w.value, kcg, vcg, slots)
+    qs_bad = qs.copy()
+    qs_bad[4] = qs[4] + 7
+    qs_bad[0] = -1
+    out4 = torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device)
+    pa.pa_prefill(out4, q, kcg, vcg, bt, cl, torch.from_numpy(qs_bad).to(q.device), w.scale, 10)
+    torch.cuda.synchronize()
+    assert torch.isnan(out4[qs[3]:]).all() and torch.isnan(out4[:qs[1]]).all()
+    assert not torch.isnan(out4[qs[1]:qs[3]]).any()
 
 
 def test_prefill_placement_invariant():
