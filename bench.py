@@ -17,8 +17,11 @@ lengths, different block placement and values; R * 131 MB >> 256 MB).
 
 Printed: one JSON line on stdout. `value` is KV-read GB/s of whole steps
 (scatter + attention, launch gaps included); `roofline` is the attention call
-alone, timed with HIP events on the launch stream; `cpu_baseline` is the fp64
-oracle on the host cores over a bounded sample of the same workload.
+alone, timed with HIP events on the launch stream (also after a 1 GiB write
+that evicts the caches: `attention_ms_cold_p50`); `stream_read` is the rate of the
+library's plain streaming-read kernel over 2 GiB, the achievable ceiling next to
+the nominal 8 TB/s; `cpu_baseline` is the fp64 oracle on the host cores (and on
+one thread) over a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -82,6 +85,10 @@ def main() -> int:
                          "(shared-prefix workloads only)")
     ap.add_argument("--partition-size", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--stream-read-mib", type=int, default=2048,
+                    help="buffer read by the streaming-read calibration kernel (0 = skip)")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="attention calls timed after a 1 GiB write evicts the caches (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -119,6 +126,7 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: 3 copies of {n} bytes")
         del src, dst
+    stream_read = stream_read_rate(dev, args.stream_read_mib << 20) if args.stream_read_mib > 0 else None
     spec = wl.SPECS[args.workload]
     psize = args.partition_size or spec.partition_size
 
@@ -204,6 +212,23 @@ def main() -> int:
     call_ms = np.array([a.elapsed_time(b) for a, b in evs])
     log(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
 
+    cold_ms = None
+    if args.cold_calls > 0:
+        # Each call after a 1 GiB write that pushes the batch out of L2 and the
+        # Infinity Cache; only the attention call is timed.
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.cold_calls)]
+        for i, (a, b) in enumerate(cevs):
+            scratch.fill_(i & 0xFF)
+            a.record()
+            attention(inputs[i % len(inputs)])
+            b.record()
+        torch.cuda.synchronize()
+        cold_ms = float(np.median([a.elapsed_time(b) for a, b in cevs]))
+        del scratch
+        log(f"[bench] cold calls: median {cold_ms * 1e3:.2f} us over {args.cold_calls}")
+
     ms_per_step = elapsed * 1e3 / args.steps
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     attn_ms = float(np.mean(call_ms))
@@ -241,6 +266,10 @@ def main() -> int:
         "seq_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
         "attention_ms_per_call": round(attn_ms, 5),
         "attention_ms_p50": round(float(np.median(call_ms)), 5),
+        "attention_ms_min": round(float(np.min(call_ms)), 5),
+        "attention_ms_cold_p50": round(cold_ms, 5) if cold_ms is not None else None,
+        "stream_read": stream_read,
+        "pct_of_stream_read": round(100.0 * achieved / stream_read["gbs"], 2) if stream_read else None,
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -386,6 +415,48 @@ def bench_prefill(args, dev) -> int:
     return 0
 
 
+def stream_read_rate(dev, nbytes: int) -> dict:
+    """The HBM read rate of pa_stream_read (the decode kernels' nontemporal 16-byte
+    loads, nothing else) over an `nbytes` buffer, best over four grid sizes, each the
+    mean of 10 launches timed with HIP events on the launch stream."""
+    import torch
+
+    import paged_kv_cache_456_amd as pa
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(7)
+    best = None
+    for wgs in (4 * cus, 8 * cus, 16 * cus, 32 * cus):
+        sink = torch.empty(64 * wgs, dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            pa.pa_stream_read(buf, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            pa.pa_stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        gbs = nbytes / (us * 1e-6) / 1e9
+        log(f"[bench] stream read {nbytes >> 20} MiB, {wgs} workgroups: {us:.1f} us = {gbs:.0f} GB/s")
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "bytes": nbytes, "workgroups": wgs, "us_per_launch": round(us, 2),
+                    "kernel": "stream_read_kernel (pa_stream_read)"}
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, kv_bytes: int, seconds: float):
     """The fp64 oracle (cache write + decode of the whole batch) on the host cores,
     repeated for about `seconds` of wall clock. Host copies are made first."""
@@ -425,9 +496,23 @@ def cpu_baseline(w, kv_bytes: int, seconds: float):
         if el >= seconds:
             break
     log(f"[bench] cpu oracle: {n} steps in {el:.2f} s")
+    # The same steps on one thread, for a fifth of the time (last: the thread
+    # count set here stays for the process).
+    n1 = 0
+    t1 = time.perf_counter()
+    while True:
+        oracle.reshape_and_cache(kn, vn, kb, vb, slots, block_size=B)
+        oracle.decode(q, kc, vc, tables, w.context_lens, w.scale, num_threads=1)
+        n1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= seconds / 5:
+            break
+    log(f"[bench] cpu oracle, 1 thread: {n1} steps in {el1:.2f} s")
     return {
         "value": round(kv_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
         "seq_steps_per_s": round(w.num_seqs * n / el, 2),
+        "value_1_thread": round(kv_bytes * n1 / el1 / 1e9, 4),
+        "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
         "sample": f"{n} full decode steps of the same batch ({w.num_seqs} sequences, cache write + "
                   f"attention, fp64, inputs in host memory), {el:.1f} s wall; device-to-host copy "
                   f"{t_copy:.2f} s not included",

@@ -386,6 +386,28 @@ int64_t pa_bm_length(const pa_block_manager* bm, int64_t seq_id);
 int64_t pa_bm_block_table(const pa_block_manager* bm, int64_t seq_id, int32_t* table_out,
                           int max_entries, int32_t pad);
 
+/*
+ * pa_stream_read -- streaming-read calibration: the HBM read rate this GPU
+ * reaches, the practical ceiling of the bandwidth-bound decode kernels.
+ *
+ * Reads each of the num_words 16-byte words at src once, with the 16-byte
+ * nontemporal loads the decode kernels use for K and V, over num_workgroups
+ * workgroups of 4 waves, and writes one 16-byte word per wave to sink: the
+ * XOR of the words that wave read. The XOR of all 4 * num_workgroups sink
+ * words equals the XOR of all words of src, whatever num_workgroups is.
+ *
+ *   src            device memory, 16-byte aligned, num_words * 16 bytes
+ *                  (may be null when num_words = 0).
+ *   sink           device memory, 16-byte aligned, 64 * num_workgroups bytes;
+ *                  every word is written (zero for a wave that read nothing).
+ *   num_workgroups 1 .. 2^20.
+ *
+ * PA_EINVAL for a negative num_words, num_workgroups out of range, a null or
+ * misaligned pointer; PA_EHIP for a launch failure. Nothing is retained.
+ */
+pa_status_t pa_stream_read(const void* src, int64_t num_words, void* sink, int num_workgroups,
+                           void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* pa_status_str(pa_status_t status);
 

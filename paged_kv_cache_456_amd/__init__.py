@@ -11,6 +11,7 @@ declared in ``include/pa.h``). This package is its thin Python binding:
                            read once per KV head, plus per-sequence suffixes
     pa_prefill             multi-token queries (a prompt or a chunk of one)
                            attending causally over the paged cache
+    pa_stream_read         streaming-read calibration (the achievable HBM read rate)
     BlockManager           the host-side block manager (pa_bm_*): block tables,
                            shared blocks, copy-on-write pairs
 """
@@ -18,5 +19,5 @@ from ._lib import (  # noqa: F401
     PA_BF16, PA_F32, BlockManager, NoSpace, PagedAttentionError, cascade_workspace, decode_workspace, load,
     pa_copy_blocks, pa_decode, pa_decode_cascade, pa_decode_cascade_workspace_size,
     pa_decode_partitioned, pa_decode_partitioned_workspace_size, pa_prefill, pa_reshape_and_cache,
-    pa_status_str, workspace_partials,
+    pa_status_str, pa_stream_read, workspace_partials,
 )

@@ -19,7 +19,7 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOSPACE = 0, 1, 2
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_partitioned",
            "pa_decode_partitioned_workspace_size", "pa_decode_cascade",
-           "pa_decode_cascade_workspace_size", "pa_prefill", "pa_status_str",
+           "pa_decode_cascade_workspace_size", "pa_prefill", "pa_stream_read", "pa_status_str",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token",
            "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_num_free_blocks", "pa_bm_length",
            "pa_bm_block_table")
@@ -48,6 +48,8 @@ def load() -> ctypes.CDLL:
     lib.pa_reshape_and_cache.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
     lib.pa_copy_blocks.restype = i32
+    lib.pa_stream_read.argtypes = [vp, i64, vp, i32, vp]
+    lib.pa_stream_read.restype = i32
     lib.pa_decode.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i64,
                               f32, vp]
     lib.pa_decode.restype = i32
@@ -159,6 +161,21 @@ def pa_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
                                block_mapping.shape[0], Hkv, D, B, NB, _dtype_code(key_cache.dtype),
                                _stream(key_cache, stream))
     _check(rc, "pa_copy_blocks")
+
+
+def pa_stream_read(src: torch.Tensor, sink: torch.Tensor,
+                   stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Read every 16-byte word of `src` (a contiguous GPU tensor of a multiple of 16
+    bytes) once; sink (uint8 [64 * W] on the GPU, W >= 1 workgroups) receives one
+    XOR word per wave. A calibration of the achievable HBM read rate."""
+    _dev(src, sink)
+    nbytes = src.numel() * src.element_size()
+    if nbytes % 16 or sink.dtype != torch.uint8 or sink.dim() != 1 or sink.numel() % 64 or \
+            not sink.numel():
+        raise ValueError("src must hold a multiple of 16 bytes and sink be uint8 [64 * W]")
+    rc = load().pa_stream_read(src.data_ptr(), nbytes // 16, sink.data_ptr(), sink.numel() // 64,
+                               _stream(src, stream))
+    _check(rc, "pa_stream_read")
 
 
 def _decode_common(out, query, key_cache, value_cache, block_tables, context_lens):

@@ -149,6 +149,19 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* key_c
     return from_hip(pa::launch_cache(p, num_tokens, static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t pa_stream_read(const void* src, int64_t num_words, void* sink, int num_workgroups,
+                           void* stream) {
+    if (num_words < 0 || num_workgroups <= 0 || num_workgroups > (1 << 20) || !sink ||
+        (num_words > 0 && !src))
+        return PA_EINVAL;
+    if ((num_words > 0 && !aligned(src, 16)) || !aligned(sink, 16))
+        return PA_EINVAL;
+    if (num_words > INT64_MAX / 16)
+        return PA_EINVAL;
+    return from_hip(pa::launch_stream_read(src, num_words, sink, num_workgroups,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
                            int64_t num_pairs, int num_kv_heads, int head_size, int block_size,
                            int64_t num_blocks, pa_dtype_t kv_dtype, void* stream) {

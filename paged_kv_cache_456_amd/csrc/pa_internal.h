@@ -185,5 +185,8 @@ hipError_t launch_cascade_prefix(const CascadeParams& p, int head_size, int num_
                                  hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_size, int out_bf16, int num_seqs,
                           int row_tiles, hipStream_t stream);
+int stream_read_waves_per_workgroup();
+hipError_t launch_stream_read(const void* src, int64_t num_words, void* sink, int num_workgroups,
+                              hipStream_t stream);
 
 }  // namespace pa

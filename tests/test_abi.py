@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import paged_kv_cache_456_amd as pa
 from paged_kv_cache_456_amd import _lib
@@ -211,3 +212,17 @@ def test_prefill_shares_decode_checks(lib, kw, expect):
 ])
 def test_prefill_checks(lib, kw, expect):
     assert prefill_call(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("args", [
+    (P, -1, P, 4), (P, 8, P, 0), (P, 8, P, (1 << 20) + 1), (0, 8, P, 4), (P, 8, 0, 4),
+    (P + 8, 8, P, 4), (P, 8, P + 4, 4), (P, 1 << 62, P, 4),
+])
+def test_stream_read_checks(lib, args):
+    src, n, sink, wgs = args
+    assert lib.pa_stream_read(src, n, sink, wgs, None) == EINVAL
+
+
+def test_stream_read_binding_checks():
+    with pytest.raises(ValueError):
+        pa.pa_stream_read(torch.zeros(16, dtype=torch.uint8), torch.zeros(64, dtype=torch.uint8))
