@@ -755,25 +755,40 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams
 }
 
 template <typename KV, int D, int GMAX, typename OUT>
+hipError_t launch_decode_grid(const DecodeParams& p, int num_seqs, int grid_partitions, int waves,
+                              hipStream_t stream) {
+    const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, waves);
+    hipLaunchKernelGGL((paged_decode_kernel<KV, D, GMAX, OUT>),
+                       dim3(p.num_kv_heads, num_seqs, grid_partitions), dim3(waves * kWave), lds,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <typename KV, int D, int GMAX, typename OUT>
 hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, int grid_partitions, int waves,
                            hipStream_t stream) {
-    if (!p.persistent) {
-        const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, waves);
-        hipLaunchKernelGGL((paged_decode_kernel<KV, D, GMAX, OUT>),
-                           dim3(p.num_kv_heads, num_seqs, grid_partitions), dim3(waves * kWave), lds,
-                           stream, p);
-        return hipGetLastError();
-    }
+    if (!p.persistent)
+        return launch_decode_grid<KV, D, GMAX, OUT>(p, num_seqs, grid_partitions, waves, stream);
     const auto kernel = paged_decode_persistent_kernel<KV, D, GMAX, OUT>;
     // Persistent: as many workgroups as the GPU keeps resident at once (never
     // more than there can be items).
     const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, waves) + persistent_lds_bytes(num_seqs);
-    int dev = 0, cus = 0, per_cu = 0;
+    int dev = 0, cus = 0, per_cu = 0, max_lds = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess)
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, waves * kWave, lds);
+        e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess)
+        return e;
+    if (lds > static_cast<size_t>(max_lds)) {
+        // The sequence list does not fit one workgroup's LDS: one workgroup
+        // per (KV head, sequence, partition) computes the same partials.
+        DecodeParams g = p;
+        g.persistent = 0;
+        return launch_decode_grid<KV, D, GMAX, OUT>(g, num_seqs, grid_partitions, waves, stream);
+    }
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, waves * kWave, lds);
     if (e != hipSuccess)
         return e;
     const int64_t bound = static_cast<int64_t>(num_seqs) * p.num_kv_heads * grid_partitions;

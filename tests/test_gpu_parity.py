@@ -161,6 +161,25 @@ def test_partitioned_mixed_lengths():
     assert torch.equal(g.out[0], torch.zeros_like(g.out[0])) and torch.isnan(g.out[4]).all()
 
 
+@pytest.mark.parametrize("S,G", [(4096, 16), (4096, 4), (4097, 4)])
+def test_sequence_cap(S, G):
+    """The persistent schedule at its sequence cap, where its sequence list fills most of
+    its LDS (with head group 16 the list and the decode tiles together may exceed one
+    workgroup's LDS, and the launch falls back to one workgroup per item), and one
+    sequence past the cap (the grid schedule): outputs match the oracle with 16-token
+    partitions (up to 3 per context, reduced) and with one partition per context."""
+    props = torch.cuda.get_device_properties(0)
+    print(f"LDS per workgroup: {getattr(props, 'shared_memory_per_block', 'unknown')}", flush=True)
+    lengths = np.random.default_rng(S + G).integers(1, 49, S).tolist()
+    spec = wl.custom_spec(lengths, 2 * G, 2, 128, torch.bfloat16, index=340 + G)
+    w = wl.make_workload(spec, device="cuda")
+    for psize in (16, 256):
+        r = oracle_step(w, partition_size=psize)
+        g = gpu_step(w, partition_size=psize)
+        check_scatter(w, g, r)
+        _report(f"S={S} G={G} P={psize}", max_abs_err(g.out, r.out), TOL[torch.bfloat16])
+
+
 def test_reduce_many_partitions():
     """Rows with more than 16 and more than 64 partitions: the combining kernel loads
     partials 16 at a time and merges them 64 at a time with rescaling; both must give
