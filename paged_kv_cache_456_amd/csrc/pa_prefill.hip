@@ -53,7 +53,9 @@ __device__ __forceinline__ void store_row_value<BF16>(void* out, int64_t idx, fl
 }
 
 template <int D, typename OUT>
-__global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPrefillWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(3)))   // 3 waves per SIMD: 162 VGPRs, no spill (D = 128)
+void prefill_kernel(PrefillParams p) {
     constexpr int ROW = D * 2;                  // bytes per token row (bf16)
     constexpr int TILE = kBlockSize * ROW;
     constexpr int CH = ROW / 16;                // 16-byte chunks per row
