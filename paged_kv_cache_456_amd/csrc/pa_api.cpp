@@ -466,7 +466,8 @@ pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query, const
     const int64_t rows = static_cast<int64_t>(max_query_len) * (num_q_heads / num_kv_heads);
     if (rows > INT32_MAX)
         return PA_EUNSUPPORTED;
-    const int64_t tiles = (rows + pa::kPrefillWaves * 16 - 1) / (pa::kPrefillWaves * 16);
+    constexpr int kTileRows = pa::kPrefillWaves * 16 * pa::kPrefillRowTiles;
+    const int64_t tiles = (rows + kTileRows - 1) / kTileRows;
     pa::PrefillParams p{};
     p.q = query;
     p.k_cache = key_cache;

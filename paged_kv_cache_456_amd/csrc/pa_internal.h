@@ -14,7 +14,8 @@ constexpr int kPartWaves = 4;    // waves per decode workgroup (partitioned)
 constexpr int kReduceThreads = 256;
 constexpr int kCascadeWaves = 4;          // 64 query rows per prefix workgroup
 constexpr int kCascadeChunkBlocks = 16;   // prefix blocks per prefix workgroup
-constexpr int kPrefillWaves = 4;          // 64 query rows per multi-token-query workgroup
+constexpr int kPrefillWaves = 4;          // waves per multi-token-query workgroup
+constexpr int kPrefillRowTiles = 2;       // 16-row tiles per wave (128 rows per workgroup)
 
 // Element tags for the KV dtype.
 struct BF16 {

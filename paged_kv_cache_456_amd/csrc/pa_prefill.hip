@@ -12,12 +12,13 @@
 // tokens 0 .. L_s - q_s + i, read through the block table. With q_s = 1 this
 // is the decode step; with q_s = L_s it is a whole prompt.
 //
-// Work decomposition: one workgroup per (64-row tile, KV head, sequence),
+// Work decomposition: one workgroup per (128-row tile, KV head, sequence),
 // where the rows of a (sequence, KV head) are its (query token, head of the
-// group) pairs, token-major, so that a tile spans 64 / G consecutive query
+// group) pairs, token-major, so that a tile spans 128 / G consecutive query
 // tokens and the K/V it reads is shared by all its rows: a dense tile for
-// MFMA. Per workgroup, 4 waves of 16 rows, per step of 32 context tokens
-// (two blocks):
+// MFMA. Per workgroup, 4 waves of two 16-row MFMA tiles each (the K loads,
+// the V transpose and the barriers of a step serve 32 rows of a wave), per
+// step of 32 context tokens (two blocks):
 //   * K tiles are loaded straight into the MFMA B-operand layout, Q^T K on
 //     v_mfma_f32_16x16x32_bf16 gives logits[row][token];
 //   * the causal mask is a select per row (token <= the row's position);
@@ -54,7 +55,7 @@ __device__ __forceinline__ void store_row_value<BF16>(void* out, int64_t idx, fl
 
 template <int D, typename OUT>
 __global__ __launch_bounds__(kPrefillWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(3)))   // 3 waves per SIMD: 162 VGPRs, no spill (D = 128)
+__attribute__((amdgpu_waves_per_eu(2)))   // 2 waves per SIMD: 246 VGPRs, no spill (D = 128)
 void prefill_kernel(PrefillParams p) {
     constexpr int ROW = D * 2;                  // bytes per token row (bf16)
     constexpr int TILE = kBlockSize * ROW;
@@ -62,12 +63,13 @@ void prefill_kernel(PrefillParams p) {
     constexpr int NQ = CH / 4;                  // K chunks per lane per tile
     constexpr int NT = D / 16;                  // 16-column output tiles
     constexpr int VITEMS = (kStepTokens / 2) * CH;   // (token pair, chunk) items of a step
-    constexpr int TROWS = kPrefillWaves * 16;        // rows per workgroup
+    constexpr int RT = kPrefillRowTiles;             // 16-row tiles per wave
+    constexpr int TROWS = kPrefillWaves * 16 * RT;   // rows per workgroup
     static_assert(VITEMS <= kPrefillWaves * kWave && (kPrefillWaves * kWave) % VITEMS == 0,
                   "one V item per thread");
 
     __shared__ __attribute__((aligned(16))) uint16_t vt[D][kVtStride];
-    __shared__ __attribute__((aligned(16))) float pl[kPrefillWaves][16][kPStride];
+    __shared__ __attribute__((aligned(16))) float pl[kPrefillWaves][16 * RT][kPStride];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -117,23 +119,25 @@ void prefill_kernel(PrefillParams p) {
         poisoned = __ballot(bad) != 0;
     }
 
-    // Rows of this wave: A-operand row r16 and output rows 4g + j.
-    const int row0 = tile0 + wave * 16;
-    u32x4 qa[NQ];
-    {
-        const int r = row0 + r16;
+    // Rows of this wave: tile t holds rows row0 + 16t + (A-operand row r16,
+    // output rows 4g + j).
+    const int row0 = tile0 + wave * 16 * RT;
+    u32x4 qa[RT][NQ];
+    int pos[RT][4];                             // causal limit of rows 4g + j of tile t
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int r = row0 + 16 * t + r16;
         const bool live = r < rows;
         const char* qp = static_cast<const char*>(p.q) + out_row(live ? r : tile0) * ROW;
 #pragma unroll
         for (int c = 0; c < NQ; ++c)
-            qa[c] = live ? *reinterpret_cast<const u32x4*>(qp + (g + 4 * c) * 16)
-                         : u32x4{0u, 0u, 0u, 0u};
-    }
-    int pos[4];                                 // causal limit of rows 4g + j
+            qa[t][c] = live ? *reinterpret_cast<const u32x4*>(qp + (g + 4 * c) * 16)
+                            : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = row0 + 4 * g + j;
-        pos[j] = r < rows ? L - nq + r / G : 0;
+        for (int j = 0; j < 4; ++j) {
+            const int rr = row0 + 16 * t + 4 * g + j;
+            pos[t][j] = rr < rows ? L - nq + rr / G : 0;
+        }
     }
     const int maxpos = L - nq + last_row / G;   // the tile reads tokens 0 .. maxpos
     const int nblk = maxpos / kBlockSize + 1;
@@ -179,16 +183,19 @@ void prefill_kernel(PrefillParams p) {
         vr[1] = *reinterpret_cast<const u32x4*>(v + ROW);
     };
 
-    float m[4], lsum[4];
-    f32x4 o[NT];
+    float m[RT][4], lsum[RT][4];
+    f32x4 o[RT][NT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        m[j] = -INFINITY;
-        lsum[j] = 0.0f;
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m[t][j] = -INFINITY;
+            lsum[t][j] = 0.0f;
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            o[t][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-        o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     load_step(0);
     for (int st = 0; st < nsteps; ++st) {
@@ -214,71 +221,80 @@ void prefill_kernel(PrefillParams p) {
         // Next step's loads go out now and land while this step computes (the
         // last step reloads itself, so that no load sits under a branch).
         load_step(min(st + 1, nsteps - 1));
-        // logits[row 4g+j][token t0 + b*16 + r16]
-        f32x4 acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
-                                                           __builtin_bit_cast(bf16x8, k0[c]), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
-                                                           __builtin_bit_cast(bf16x8, k1[c]), acc1, 0, 0, 0);
+        for (int t = 0; t < RT; ++t) {
+            // logits[row 4g+j of tile t][token t0 + b*16 + r16]
+            f32x4 acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[t][c]),
+                                                               __builtin_bit_cast(bf16x8, k0[c]), acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[t][c]),
+                                                               __builtin_bit_cast(bf16x8, k1[c]), acc1, 0, 0, 0);
+            }
+            float alpha[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // Masked logits are dropped by select (they may be NaN in block tails).
+                const float x0 = t0 + r16 <= pos[t][j] ? acc0[j] * p.scale_log2 : -INFINITY;
+                const float x1 = t0 + 16 + r16 <= pos[t][j] ? acc1[j] * p.scale_log2 : -INFINITY;
+                // Token 0 is visible to every row, so the running max is finite
+                // from the first step on.
+                const float mn = fmaxf(m[t][j], row_max16(fmaxf(x0, x1)));
+                alpha[j] = __builtin_amdgcn_exp2f(m[t][j] - mn);
+                const float p0 = __builtin_amdgcn_exp2f(x0 - mn);
+                const float p1 = __builtin_amdgcn_exp2f(x1 - mn);
+                lsum[t][j] = lsum[t][j] * alpha[j] + p0 + p1;
+                m[t][j] = mn;
+                pl[wave][16 * t + 4 * g + j][r16] = p0;
+                pl[wave][16 * t + 4 * g + j][16 + r16] = p1;
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[t][n][j] *= alpha[j];
         }
-        float alpha[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // Masked logits are dropped by select (they may be NaN in block tails).
-            const float x0 = t0 + r16 <= pos[j] ? acc0[j] * p.scale_log2 : -INFINITY;
-            const float x1 = t0 + 16 + r16 <= pos[j] ? acc1[j] * p.scale_log2 : -INFINITY;
-            // Token 0 is visible to every row, so the running max is finite
-            // from the first step on.
-            const float mn = fmaxf(m[j], row_max16(fmaxf(x0, x1)));
-            alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
-            const float p0 = __builtin_amdgcn_exp2f(x0 - mn);
-            const float p1 = __builtin_amdgcn_exp2f(x1 - mn);
-            lsum[j] = lsum[j] * alpha[j] + p0 + p1;
-            m[j] = mn;
-            pl[wave][4 * g + j][r16] = p0;
-            pl[wave][4 * g + j][16 + r16] = p1;
-        }
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[n][j] *= alpha[j];
         lds_barrier();                          // P of every wave and all of V^T are in LDS
         // P as the A operand (row r16, tokens 8g..8g+7), split into bf16 hi + lo.
-        u16x8 phi, plo;
-        {
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(&pl[wave][r16][8 * g]);
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(&pl[wave][r16][8 * g + 4]);
+        u16x8 phi[RT], plo[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(&pl[wave][16 * t + r16][8 * g]);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(&pl[wave][16 * t + r16][8 * g + 4]);
             const float pv[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            split_bf16x8(pv, phi, plo);
+            split_bf16x8(pv, phi[t], plo[t]);
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const u16x8 vb = *reinterpret_cast<const u16x8*>(&vt[n * 16 + r16][8 * g]);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, phi),
-                                                           __builtin_bit_cast(bf16x8, vb), o[n], 0, 0, 0);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo),
-                                                           __builtin_bit_cast(bf16x8, vb), o[n], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, phi[t]),
+                                                                  __builtin_bit_cast(bf16x8, vb), o[t][n], 0, 0, 0);
+                o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo[t]),
+                                                                  __builtin_bit_cast(bf16x8, vb), o[t][n], 0, 0, 0);
+            }
         }
         lds_barrier();                          // LDS free for the next step
     }
 
-    // Output rows 4g+j of the wave, columns n*16 + r16.
+    // Output rows 4g+j of each tile, columns n*16 + r16.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float srow = row_sum16(lsum[j]);
-        const int r = row0 + 4 * g + j;
-        if (r >= rows)
-            continue;
-        const int64_t base = out_row(r) * D;
-        const float inv = 1.0f / srow;
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-            store_row_value<OUT>(p.out, base + n * 16 + r16,
-                                 poisoned ? __builtin_nanf("") : o[n][j] * inv);
-    }
+        for (int j = 0; j < 4; ++j) {
+            const float srow = row_sum16(lsum[t][j]);
+            const int r = row0 + 16 * t + 4 * g + j;
+            if (r >= rows)
+                continue;
+            const int64_t base = out_row(r) * D;
+            const float inv = 1.0f / srow;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                store_row_value<OUT>(p.out, base + n * 16 + r16,
+                                     poisoned ? __builtin_nanf("") : o[t][n][j] * inv);
+        }
 }
 
 }  // namespace
