@@ -7,14 +7,15 @@
 // and V are the same for all S * G query rows that read that head, so the
 // prefix part of decode attention is a dense product: logits = Q K^T over
 // [S * G rows] x [prefix tokens], and P V. This kernel computes it once per
-// (KV head, 64-row tile, prefix chunk) on MFMA, and writes per-row partials
+// (KV head, 128-row tile, prefix chunk) on MFMA, and writes per-row partials
 // (max m, sum s, normalised output o) of the chunk into the partition slots
 // of the partitioned decode's workspace; the suffix of each sequence is
 // decoded by the paged kernel and the log-sum-exp reduce combines both, so
 // the result is the same attention as a plain decode over the whole context.
 //
-// Per workgroup (4 waves, 16 query rows each), per step of 32 prefix tokens
-// (two blocks):
+// Per workgroup (4 waves of two 16-row MFMA tiles each: a wave's K loads,
+// the V transpose and the barriers of a step serve 32 query rows), per step
+// of 32 prefix tokens (two blocks):
 //   * K tiles are loaded straight into the MFMA B-operand layout (token =
 //     lane % 16), Q^T K on v_mfma_f32_16x16x32_bf16 gives logits[row][token];
 //   * online softmax per row (running max and sum, base 2); the row max is a
@@ -36,19 +37,22 @@ constexpr int kVtStride = kStepTokens + 8;      // bf16 per transposed V row (80
 constexpr int kPStride = kStepTokens + 4;       // floats per P row in LDS (144 bytes)
 
 template <int D>
-__global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(CascadeParams p) {
+__global__ __launch_bounds__(kCascadeWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(2)))   // 2 waves per SIMD: 246 VGPRs, no spill (D = 128)
+void cascade_prefix_kernel(CascadeParams p) {
     constexpr int ROW = D * 2;                  // bytes per token row (bf16)
     constexpr int TILE = kBlockSize * ROW;
     constexpr int CH = ROW / 16;                // 16-byte chunks per row
     constexpr int NQ = CH / 4;                  // K chunks per lane per tile
     constexpr int NT = D / 16;                  // 16-column output tiles
     constexpr int VITEMS = (kStepTokens / 2) * CH;   // (token pair, chunk) items of a step
+    constexpr int RT = kCascadeRowTiles;             // 16-row tiles per wave
     static_assert(VITEMS <= kCascadeWaves * kWave && (kCascadeWaves * kWave) % VITEMS == 0,
                   "one V item per thread");
     static_assert(kCascadeChunkBlocks <= kWave, "a chunk's block ids fit one per lane");
 
     __shared__ __attribute__((aligned(16))) uint16_t vt[D][kVtStride];
-    __shared__ __attribute__((aligned(16))) float pl[kCascadeWaves][16][kPStride];
+    __shared__ __attribute__((aligned(16))) float pl[kCascadeWaves][16 * RT][kPStride];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -58,20 +62,21 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
     const int chunk = blockIdx.z;
     const int G = p.group, Hq = p.num_q_heads, Hkv = p.num_kv_heads;
     const int rows = p.num_seqs * G;
-    const int row0 = blockIdx.y * (kCascadeWaves * 16) + wave * 16;
+    const int row0 = blockIdx.y * (kCascadeWaves * 16 * RT) + wave * 16 * RT;
 
-    // Query rows of this wave as the MFMA A operand: lane row r16.
-    u32x4 qa[NQ];
-    {
-        const int r = row0 + r16;
+    // Query rows of this wave as the MFMA A operand: tile t, lane row r16.
+    u32x4 qa[RT][NQ];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int r = row0 + 16 * t + r16;
         const bool live = r < rows;
         const int seq = live ? r / G : 0, hh = live ? r - (r / G) * G : 0;
         const char* qp = static_cast<const char*>(p.q) +
                          ((int64_t)seq * Hq + (int64_t)kvh * G + hh) * ROW;
 #pragma unroll
         for (int c = 0; c < NQ; ++c)
-            qa[c] = live ? *reinterpret_cast<const u32x4*>(qp + (g + 4 * c) * 16)
-                         : u32x4{0u, 0u, 0u, 0u};
+            qa[t][c] = live ? *reinterpret_cast<const u32x4*>(qp + (g + 4 * c) * 16)
+                            : u32x4{0u, 0u, 0u, 0u};
     }
 
     // The chunk's prefix block ids (row 0 of the tables), one per lane. An id
@@ -112,16 +117,19 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
         vr[1] = *reinterpret_cast<const u32x4*>(v + ROW);
     };
 
-    float m[4], lsum[4];
-    f32x4 o[NT];
+    float m[RT][4], lsum[RT][4];
+    f32x4 o[RT][NT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        m[j] = -INFINITY;
-        lsum[j] = 0.0f;
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m[t][j] = -INFINITY;
+            lsum[t][j] = 0.0f;
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            o[t][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-        o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     load_step(0);
     for (int st = 0; st < nsteps; ++st) {
@@ -145,73 +153,82 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
         // Next step's loads go out now and land while this step computes (the
         // last step reloads itself, so that no load sits under a branch).
         load_step(min(st + 1, nsteps - 1));
-        // logits[row 4g+j][token b*16 + r16]
-        f32x4 acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
-                                                           __builtin_bit_cast(bf16x8, k0[c]), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[c]),
-                                                           __builtin_bit_cast(bf16x8, k1[c]), acc1, 0, 0, 0);
+        for (int t = 0; t < RT; ++t) {
+            // logits[row 4g+j of tile t][token b*16 + r16]
+            f32x4 acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[t][c]),
+                                                               __builtin_bit_cast(bf16x8, k0[c]), acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[t][c]),
+                                                               __builtin_bit_cast(bf16x8, k1[c]), acc1, 0, 0, 0);
+            }
+            float alpha[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x0 = acc0[j] * p.scale_log2;
+                const float x1 = pair ? acc1[j] * p.scale_log2 : -INFINITY;
+                const float mn = fmaxf(m[t][j], row_max16(fmaxf(x0, x1)));
+                alpha[j] = __builtin_amdgcn_exp2f(m[t][j] - mn);
+                const float p0 = __builtin_amdgcn_exp2f(x0 - mn);
+                const float p1 = __builtin_amdgcn_exp2f(x1 - mn);
+                lsum[t][j] = lsum[t][j] * alpha[j] + p0 + p1;
+                m[t][j] = mn;
+                pl[wave][16 * t + 4 * g + j][r16] = p0;
+                pl[wave][16 * t + 4 * g + j][16 + r16] = p1;
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[t][n][j] *= alpha[j];
         }
-        float alpha[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float x0 = acc0[j] * p.scale_log2;
-            const float x1 = pair ? acc1[j] * p.scale_log2 : -INFINITY;
-            const float mn = fmaxf(m[j], row_max16(fmaxf(x0, x1)));
-            alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
-            const float p0 = __builtin_amdgcn_exp2f(x0 - mn);
-            const float p1 = __builtin_amdgcn_exp2f(x1 - mn);
-            lsum[j] = lsum[j] * alpha[j] + p0 + p1;
-            m[j] = mn;
-            pl[wave][4 * g + j][r16] = p0;
-            pl[wave][4 * g + j][16 + r16] = p1;
-        }
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[n][j] *= alpha[j];
         lds_barrier();                     // P of every wave and all of V^T are in LDS
         // P as the A operand (row r16, tokens 8g..8g+7), split into bf16 hi + lo.
-        u16x8 phi, plo;
-        {
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(&pl[wave][r16][8 * g]);
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(&pl[wave][r16][8 * g + 4]);
+        u16x8 phi[RT], plo[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(&pl[wave][16 * t + r16][8 * g]);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(&pl[wave][16 * t + r16][8 * g + 4]);
             const float pv[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            split_bf16x8(pv, phi, plo);
+            split_bf16x8(pv, phi[t], plo[t]);
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const u16x8 vb = *reinterpret_cast<const u16x8*>(&vt[n * 16 + r16][8 * g]);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, phi),
-                                                           __builtin_bit_cast(bf16x8, vb), o[n], 0, 0, 0);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo),
-                                                           __builtin_bit_cast(bf16x8, vb), o[n], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, phi[t]),
+                                                                  __builtin_bit_cast(bf16x8, vb), o[t][n], 0, 0, 0);
+                o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo[t]),
+                                                                  __builtin_bit_cast(bf16x8, vb), o[t][n], 0, 0, 0);
+            }
         }
         lds_barrier();                     // LDS free for the next step
     }
 
-    // Row partials of this chunk: rows 4g+j of the wave, columns n*16 + r16.
+    // Row partials of this chunk: rows 4g+j of each tile, columns n*16 + r16.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float srow = row_sum16(lsum[j]);
-        const int r = row0 + 4 * g + j;
-        if (r >= rows)
-            continue;
-        const int seq = r / G, hh = r - (r / G) * G;
-        const int64_t pi = ((int64_t)seq * Hq + (int64_t)kvh * G + hh) * p.part_stride +
-                           p.slot_base + chunk;
-        const float inv = 1.0f / srow;
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-            p.part_out[pi * D + n * 16 + r16] = poisoned ? __builtin_nanf("") : o[n][j] * inv;
-        if (r16 == 0) {
-            p.part_max[pi] = poisoned ? 0.0f : m[j] * kLn2;
-            p.part_sum[pi] = poisoned ? __builtin_nanf("") : srow;
+        for (int j = 0; j < 4; ++j) {
+            const float srow = row_sum16(lsum[t][j]);
+            const int r = row0 + 16 * t + 4 * g + j;
+            if (r >= rows)
+                continue;
+            const int seq = r / G, hh = r - (r / G) * G;
+            const int64_t pi = ((int64_t)seq * Hq + (int64_t)kvh * G + hh) * p.part_stride +
+                               p.slot_base + chunk;
+            const float inv = 1.0f / srow;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                p.part_out[pi * D + n * 16 + r16] = poisoned ? __builtin_nanf("") : o[t][n][j] * inv;
+            if (r16 == 0) {
+                p.part_max[pi] = poisoned ? 0.0f : m[t][j] * kLn2;
+                p.part_sum[pi] = poisoned ? __builtin_nanf("") : srow;
+            }
         }
-    }
 }
 
 }  // namespace
@@ -219,7 +236,8 @@ __global__ __launch_bounds__(kCascadeWaves * kWave) void cascade_prefix_kernel(C
 hipError_t launch_cascade_prefix(const CascadeParams& p, int head_size, int num_chunks,
                                  hipStream_t stream) {
     const int rows = p.num_seqs * p.group;
-    const dim3 grid(p.num_kv_heads, (rows + kCascadeWaves * 16 - 1) / (kCascadeWaves * 16), num_chunks);
+    constexpr int kTileRows = kCascadeWaves * 16 * kCascadeRowTiles;
+    const dim3 grid(p.num_kv_heads, (rows + kTileRows - 1) / kTileRows, num_chunks);
     if (head_size == 64)
         hipLaunchKernelGGL(cascade_prefix_kernel<64>, grid, dim3(kCascadeWaves * kWave), 0, stream, p);
     else
