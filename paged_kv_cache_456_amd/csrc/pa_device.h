@@ -83,5 +83,22 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroups are dealt to the GPU's 8 XCDs round-robin by their flattened id
+// (x fastest). For a grid of n workgroups made of groups of `group` logical
+// neighbours (tiles that read the same K/V), this maps flattened id `id` to
+// a logical id such that every group runs on one XCD, whose L2 then serves
+// its shared reads, and consecutive groups go to different XCDs (so the work
+// stays spread over all of them). It is a bijection of [0, n) when the group
+// count is a multiple of 8; otherwise the identity is returned. Results never
+// depend on it.
+__device__ __forceinline__ int64_t xcd_grouped(int64_t id, int64_t n, int64_t group) {
+    constexpr int64_t kXcds = 8;
+    const int64_t groups = n / group;
+    if (groups * group != n || groups % kXcds != 0)
+        return id;
+    const int64_t x = id % kXcds, k = id / kXcds;
+    return (x + kXcds * (k / group)) * group + k % group;
+}
+
 }  // namespace dev
 }  // namespace pa

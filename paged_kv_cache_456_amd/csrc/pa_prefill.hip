@@ -16,9 +16,11 @@
 // where the rows of a (sequence, KV head) are its (query token, head of the
 // group) pairs, token-major, so that a tile spans 128 / G consecutive query
 // tokens and the K/V it reads is shared by all its rows: a dense tile for
-// MFMA. Per workgroup, 4 waves of two 16-row MFMA tiles each (the K loads,
-// the V transpose and the barriers of a step serve 32 rows of a wave), per
-// step of 32 context tokens (two blocks):
+// MFMA. The row tiles of one (sequence, KV head) run on one XCD, so that its
+// L2 serves their shared K/V, and successive (sequence, KV head) pairs go to
+// different XCDs. Per workgroup, 4 waves of two 16-row MFMA tiles each (the K
+// loads, the V transpose and the barriers of a step serve 32 rows of a wave),
+// per step of 32 context tokens (two blocks):
 //   * K tiles are loaded straight into the MFMA B-operand layout, Q^T K on
 //     v_mfma_f32_16x16x32_bf16 gives logits[row][token];
 //   * the causal mask is a select per row (token <= the row's position);
@@ -75,8 +77,15 @@ void prefill_kernel(PrefillParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int g = lane >> 4;
     const int r16 = lane & 15;
-    const int kvh = blockIdx.y;
-    const int s = blockIdx.z;
+    // Logical tile: the row tiles of one (sequence, KV head) form a group that
+    // runs on one XCD, whose L2 then serves their shared K/V.
+    const int64_t nwg = static_cast<int64_t>(gridDim.x) * gridDim.y * gridDim.z;
+    const int64_t lid = xcd_grouped(
+        blockIdx.x + static_cast<int64_t>(gridDim.x) * (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z),
+        nwg, gridDim.x);
+    const int tile = static_cast<int>(lid % gridDim.x);
+    const int kvh = static_cast<int>((lid / gridDim.x) % gridDim.y);
+    const int s = static_cast<int>(lid / (static_cast<int64_t>(gridDim.x) * gridDim.y));
     const int G = p.group, Hq = p.num_q_heads, Hkv = p.num_kv_heads;
     const int q0 = p.query_start[s];
     const int64_t q_end = p.query_start[s + 1];
@@ -88,7 +97,7 @@ void prefill_kernel(PrefillParams p) {
     // Rows computed: the first min(nq, max_query_len) query tokens, every head
     // of the group (none when the sequence brings no rows).
     const int rows = min(nq, p.max_query_len) * G;
-    const int tile0 = blockIdx.x * TROWS;
+    const int tile0 = tile * TROWS;
     if (tile0 >= rows)
         return;
     const int L = p.context_lens[s];
