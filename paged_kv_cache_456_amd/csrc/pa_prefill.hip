@@ -21,7 +21,9 @@
 // different XCDs. Per workgroup, 4 waves of two 16-row MFMA tiles each (the K
 // loads, the V transpose and the barriers of a step serve 32 rows of a wave),
 // per step of 32 context tokens (two blocks):
-//   * K tiles are loaded straight into the MFMA B-operand layout, Q^T K on
+//   * the step's K is loaded once per workgroup (each thread a share of its
+//     16-byte chunks) into LDS, rows XOR-swizzled so that reads in the MFMA
+//     B-operand layout are free of bank conflicts; Q^T K on
 //     v_mfma_f32_16x16x32_bf16 gives logits[row][token];
 //   * the causal mask is a select per row (token <= the row's position);
 //   * online softmax per row (running max and sum, base 2);
@@ -30,6 +32,8 @@
 //   * V is written to LDS transposed; tokens past the tile's last position
 //     (the block tail, which may hold anything) are written as zeros, so that
 //     they contribute exactly nothing to P.V on MFMA;
+//   * K and V^T live in two LDS buffers used on alternate steps, so one
+//     barrier per step suffices;
 //   * the next step's K and V are requested before this step computes.
 // Block ids come from a per-lane register holding 64 consecutive table
 // entries, reloaded every 64 blocks.
@@ -57,7 +61,7 @@ __device__ __forceinline__ void store_row_value<BF16>(void* out, int64_t idx, fl
 
 template <int D, typename OUT>
 __global__ __launch_bounds__(kPrefillWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(2)))   // 2 waves per SIMD: 246 VGPRs, no spill (D = 128)
+__attribute__((amdgpu_waves_per_eu(2)))   // 2 waves per SIMD: 234 VGPRs, no spill (D = 128)
 void prefill_kernel(PrefillParams p) {
     constexpr int ROW = D * 2;                  // bytes per token row (bf16)
     constexpr int TILE = kBlockSize * ROW;
@@ -70,7 +74,16 @@ void prefill_kernel(PrefillParams p) {
     static_assert(VITEMS <= kPrefillWaves * kWave && (kPrefillWaves * kWave) % VITEMS == 0,
                   "one V item per thread");
 
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D][kVtStride];
+    constexpr int KITEMS = kStepTokens * CH;         // 16-byte K chunks of a step
+    constexpr int KPT = KITEMS / (kPrefillWaves * kWave);   // K chunks per thread
+    static_assert(KPT >= 1 && KITEMS % (kPrefillWaves * kWave) == 0, "whole K chunks per thread");
+    // K and V^T of a step, two buffers each, alternating per step: a buffer is
+    // written again two steps later, after a barrier that every wave passes
+    // only once done with it. K rows are kept with their 16-byte chunks
+    // XOR-swizzled by the row (chunk j of token t at slot j ^ (t mod CH)), so
+    // that the B-operand reads (16 tokens, one chunk) hit 16 different banks.
+    __shared__ __attribute__((aligned(16))) u32x4 kl[2][KITEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt2[2][D][kVtStride];
     __shared__ __attribute__((aligned(16))) float pl[kPrefillWaves][16 * RT][kPStride];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -173,20 +186,29 @@ void prefill_kernel(PrefillParams p) {
         return __builtin_amdgcn_readlane(ids, b - ids_base);
     };
 
-    // Loads of step st: the K tiles of its two blocks (a lone last block is
-    // read twice; its second copy lies past maxpos and is masked) in the
-    // B-operand layout, and this thread's V pair.
-    u32x4 kt[2][NQ], vr[2];
+    // K chunks of this thread: item q = threadIdx.x + k * threads is chunk
+    // q % CH of token q / CH of the step (block (q / CH) / 16, the same for a
+    // whole wave), stored at its swizzled slot.
+    int kslot[KPT], koff[KPT], kblk[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+        const int q = threadIdx.x + k * kPrefillWaves * kWave;
+        const int t = q / CH, j = q % CH;
+        kslot[k] = t * CH + (j ^ (t & (CH - 1)));
+        kblk[k] = t >> 4;
+        koff[k] = (t & 15) * ROW + j * 16;
+    }
+    // Loads of step st: this thread's K chunks of its two blocks (a lone last
+    // block is read twice; its second copy lies past maxpos and is masked) and
+    // its V pair.
+    u32x4 kq[KPT], vr[2];
     auto load_step = [&](int st) {
         const int id0 = id_of(2 * st);
         const int id1 = id_of(min(2 * st + 1, nblk - 1));
-        const char* k0 = kbase + (int64_t)id0 * blk_stride + r16 * ROW + g * 16;
-        const char* k1 = kbase + (int64_t)id1 * blk_stride + r16 * ROW + g * 16;
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            kt[0][c] = *reinterpret_cast<const u32x4*>(k0 + 64 * c);
-            kt[1][c] = *reinterpret_cast<const u32x4*>(k1 + 64 * c);
-        }
+        for (int k = 0; k < KPT; ++k)
+            kq[k] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(kblk[k] ? id1 : id0) * blk_stride +
+                                                    koff[k]);
         const char* v = vbase + (int64_t)(vblk ? id1 : id0) * blk_stride + voff;
         vr[0] = *reinterpret_cast<const u32x4*>(v);
         vr[1] = *reinterpret_cast<const u32x4*>(v + ROW);
@@ -209,8 +231,13 @@ void prefill_kernel(PrefillParams p) {
     load_step(0);
     for (int st = 0; st < nsteps; ++st) {
         const int t0 = st * kStepTokens;
-        // V of the step, transposed into LDS (two adjacent tokens per 32-bit
-        // word); tokens past maxpos become zeros.
+        const int buf = st & 1;
+        auto& vt = vt2[buf];
+        // K of the step into LDS; V transposed into LDS (two adjacent tokens
+        // per 32-bit word), tokens past maxpos written as zeros.
+#pragma unroll
+        for (int k = 0; k < KPT; ++k)
+            kl[buf][kslot[k]] = kq[k];
         {
             const bool za = t0 + 2 * tp > maxpos, zb = t0 + 2 * tp + 1 > maxpos;
             uint32_t* col = reinterpret_cast<uint32_t*>(&vt[vc * 8][2 * tp]);
@@ -221,15 +248,18 @@ void prefill_kernel(PrefillParams p) {
                 col[(2 * e + 1) * (kVtStride / 2)] = (a >> 16) | (b & 0xFFFF0000u);
             }
         }
-        u32x4 k0[NQ], k1[NQ];
-#pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            k0[c] = kt[0][c];
-            k1[c] = kt[1][c];
-        }
         // Next step's loads go out now and land while this step computes (the
         // last step reloads itself, so that no load sits under a branch).
         load_step(min(st + 1, nsteps - 1));
+        lds_barrier();                          // K and V^T of the step are in LDS
+        // K as the B operand: token r16 of each block, chunks g + 4c.
+        u32x4 k0[NQ], k1[NQ];
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            const int cc = g + 4 * c;
+            k0[c] = kl[buf][r16 * CH + (cc ^ (r16 & (CH - 1)))];
+            k1[c] = kl[buf][(16 + r16) * CH + (cc ^ ((16 + r16) & (CH - 1)))];
+        }
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             // logits[row 4g+j of tile t][token t0 + b*16 + r16]
@@ -264,7 +294,10 @@ void prefill_kernel(PrefillParams p) {
                 for (int j = 0; j < 4; ++j)
                     o[t][n][j] *= alpha[j];
         }
-        lds_barrier();                          // P of every wave and all of V^T are in LDS
+        // This wave's P (written and read by this wave only) is in LDS.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // P as the A operand (row r16, tokens 8g..8g+7), split into bf16 hi + lo.
         u16x8 phi[RT], plo[RT];
 #pragma unroll
@@ -285,7 +318,6 @@ void prefill_kernel(PrefillParams p) {
                                                                   __builtin_bit_cast(bf16x8, vb), o[t][n], 0, 0, 0);
             }
         }
-        lds_barrier();                          // LDS free for the next step
     }
 
     // Output rows 4g+j of each tile, columns n*16 + r16.
