@@ -16,15 +16,19 @@
 // Per workgroup (4 waves of two 16-row MFMA tiles each: a wave's K loads,
 // the V transpose and the barriers of a step serve 32 query rows), per step
 // of 32 prefix tokens (two blocks):
-//   * K tiles are loaded straight into the MFMA B-operand layout (token =
-//     lane % 16), Q^T K on v_mfma_f32_16x16x32_bf16 gives logits[row][token];
+//   * the step's K is loaded once per workgroup into LDS (rows XOR-swizzled
+//     so that reads in the MFMA B-operand layout, token = lane % 16, are free
+//     of bank conflicts); Q^T K on v_mfma_f32_16x16x32_bf16 gives
+//     logits[row][token];
 //   * online softmax per row (running max and sum, base 2); the row max is a
 //     16-lane DPP row reduction;
 //   * P goes through LDS into the A-operand layout and is split into a bf16
 //     high part and a bf16 remainder, so P.V keeps about 16 bits of P;
 //   * V is written to LDS transposed (token-contiguous rows, padded so that
 //     the B-operand reads are conflict-free) and P.V runs on MFMA with the
-//     output rows in the same lanes as the softmax state.
+//     output rows in the same lanes as the softmax state;
+//   * K and V^T live in two LDS buffers used on alternate steps, so one
+//     barrier per step suffices.
 #include "pa_device.h"
 
 namespace pa {
@@ -38,7 +42,7 @@ constexpr int kPStride = kStepTokens + 4;       // floats per P row in LDS (144 
 
 template <int D>
 __global__ __launch_bounds__(kCascadeWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(2)))   // 2 waves per SIMD: 246 VGPRs, no spill (D = 128)
+__attribute__((amdgpu_waves_per_eu(2)))   // 2 waves per SIMD: 247 VGPRs, no spill (D = 128)
 void cascade_prefix_kernel(CascadeParams p) {
     constexpr int ROW = D * 2;                  // bytes per token row (bf16)
     constexpr int TILE = kBlockSize * ROW;
@@ -51,7 +55,15 @@ void cascade_prefix_kernel(CascadeParams p) {
                   "one V item per thread");
     static_assert(kCascadeChunkBlocks <= kWave, "a chunk's block ids fit one per lane");
 
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D][kVtStride];
+    constexpr int KITEMS = kStepTokens * CH;         // 16-byte K chunks of a step
+    constexpr int KPT = KITEMS / (kCascadeWaves * kWave);   // K chunks per thread
+    static_assert(KPT >= 1 && KITEMS % (kCascadeWaves * kWave) == 0, "whole K chunks per thread");
+    // K and V^T of a step, two buffers each, alternating per step (a buffer is
+    // written again two steps later, after a barrier every wave passes only
+    // once done with it); K rows XOR-swizzled (chunk j of token t at slot
+    // j ^ (t mod CH)) so that the B-operand reads hit 16 different banks.
+    __shared__ __attribute__((aligned(16))) u32x4 kl[2][KITEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt2[2][D][kVtStride];
     __shared__ __attribute__((aligned(16))) float pl[kCascadeWaves][16 * RT][kPStride];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -98,20 +110,29 @@ void cascade_prefix_kernel(CascadeParams p) {
     const int vblk = tp >> 3;                   // which block of the step
     const int voff = (2 * tp - 16 * vblk) * ROW + vc * 16;
 
-    // Loads of step st: the K tiles of its two blocks (a lone last block is
-    // read twice and masked) in the B-operand layout, and this thread's V pair.
-    u32x4 kt[2][NQ], vr[2];
+    // K chunks of this thread: item q = threadIdx.x + k * threads is chunk
+    // q % CH of token q / CH of the step (block (q / CH) / 16), stored at its
+    // swizzled slot.
+    int kslot[KPT], koff[KPT], kblk[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+        const int q = threadIdx.x + k * kCascadeWaves * kWave;
+        const int t = q / CH, j = q % CH;
+        kslot[k] = t * CH + (j ^ (t & (CH - 1)));
+        kblk[k] = t >> 4;
+        koff[k] = (t & 15) * ROW + j * 16;
+    }
+    // Loads of step st: this thread's K chunks of its two blocks (a lone last
+    // block is read twice and masked) and its V pair.
+    u32x4 kq[KPT], vr[2];
     auto load_step = [&](int st) {
         const int b0 = 2 * st, b1 = min(2 * st + 1, nblk - 1);
         const int id0 = __builtin_amdgcn_readlane(id_l, b0);
         const int id1 = __builtin_amdgcn_readlane(id_l, b1);
-        const char* k0 = kbase + (int64_t)id0 * blk_stride + r16 * ROW + g * 16;
-        const char* k1 = kbase + (int64_t)id1 * blk_stride + r16 * ROW + g * 16;
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            kt[0][c] = *reinterpret_cast<const u32x4*>(k0 + 64 * c);
-            kt[1][c] = *reinterpret_cast<const u32x4*>(k1 + 64 * c);
-        }
+        for (int k = 0; k < KPT; ++k)
+            kq[k] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(kblk[k] ? id1 : id0) * blk_stride +
+                                                    koff[k]);
         const char* v = vbase + (int64_t)(vblk ? id1 : id0) * blk_stride + voff;
         vr[0] = *reinterpret_cast<const u32x4*>(v);
         vr[1] = *reinterpret_cast<const u32x4*>(v + ROW);
@@ -134,7 +155,13 @@ void cascade_prefix_kernel(CascadeParams p) {
     load_step(0);
     for (int st = 0; st < nsteps; ++st) {
         const bool pair = 2 * st + 1 < nblk;
-        // V of the step, transposed into LDS: two adjacent tokens per 32-bit word.
+        const int buf = st & 1;
+        auto& vt = vt2[buf];
+        // K of the step into LDS; V transposed into LDS (two adjacent tokens
+        // per 32-bit word).
+#pragma unroll
+        for (int k = 0; k < KPT; ++k)
+            kl[buf][kslot[k]] = kq[k];
         {
             uint32_t* col = reinterpret_cast<uint32_t*>(&vt[vc * 8][2 * tp]);
 #pragma unroll
@@ -144,15 +171,18 @@ void cascade_prefix_kernel(CascadeParams p) {
                 col[(2 * e + 1) * (kVtStride / 2)] = (a >> 16) | (b & 0xFFFF0000u);
             }
         }
-        u32x4 k0[NQ], k1[NQ];
-#pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            k0[c] = kt[0][c];
-            k1[c] = kt[1][c];
-        }
         // Next step's loads go out now and land while this step computes (the
         // last step reloads itself, so that no load sits under a branch).
         load_step(min(st + 1, nsteps - 1));
+        lds_barrier();                     // K and V^T of the step are in LDS
+        // K as the B operand: token r16 of each block, chunks g + 4c.
+        u32x4 k0[NQ], k1[NQ];
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            const int cc = g + 4 * c;
+            k0[c] = kl[buf][r16 * CH + (cc ^ (r16 & (CH - 1)))];
+            k1[c] = kl[buf][(16 + r16) * CH + (cc ^ ((16 + r16) & (CH - 1)))];
+        }
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             // logits[row 4g+j of tile t][token b*16 + r16]
@@ -184,7 +214,10 @@ void cascade_prefix_kernel(CascadeParams p) {
                 for (int j = 0; j < 4; ++j)
                     o[t][n][j] *= alpha[j];
         }
-        lds_barrier();                     // P of every wave and all of V^T are in LDS
+        // This wave's P (written and read by this wave only) is in LDS.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // P as the A operand (row r16, tokens 8g..8g+7), split into bf16 hi + lo.
         u16x8 phi[RT], plo[RT];
 #pragma unroll
@@ -205,7 +238,6 @@ void cascade_prefix_kernel(CascadeParams p) {
                                                                   __builtin_bit_cast(bf16x8, vb), o[t][n], 0, 0, 0);
             }
         }
-        lds_barrier();                     // LDS free for the next step
     }
 
     // Row partials of this chunk: rows 4g+j of each tile, columns n*16 + r16.
