@@ -43,7 +43,12 @@
  *  t < L = context_lens[s] (the pages give no formula; this is standard
  *  scaled dot-product softmax attention of the new token over its context):
  *      l_t = scale * q[s][h] . K_t,   w_t = softmax_t(l_t),   out = sum_t w_t V_t
- *  Arithmetic is fp32 (bf16 inputs are exact in fp32). L = 0 gives a zero row.
+ *  Accumulation is fp32 everywhere (bf16 inputs are exact in fp32). In the
+ *  decode calls the softmax weights P stay fp32 through P.V. The dense-tile
+ *  calls (the shared-prefix part of pa_decode_cascade, and pa_prefill) run
+ *  P.V on bf16 matrix cores with P split into a bf16 high part plus the bf16
+ *  rounding of the remainder, which keeps about 16 bits of each weight.
+ *  L = 0 gives a zero row.
  *
  *  Pointers.   All data pointers are DEVICE pointers, 16-byte aligned, owned
  *              by the caller and kept alive until the work on `stream` has
@@ -62,10 +67,12 @@
  *                PA_ENOSPACE      (block manager) no free block for the request
  *              Device-resident inputs are not copied to the host. The kernels
  *              check them anyway and never touch memory outside the pools:
- *              a sequence whose context is longer than its table (or than
- *              max_context_len), or whose table reaches a block id outside
- *              [0, NB), gets an all-NaN output row; a slot outside the pool is
- *              skipped by the cache write.
+ *              a sequence whose context is longer than its table (16 * MB
+ *              tokens) or, in the partitioned calls, longer than
+ *              ceil(max_context_len / partition_size) * partition_size tokens,
+ *              or whose table reaches a block id outside [0, NB), gets an
+ *              all-NaN output row; a slot outside the pool is skipped by the
+ *              cache write.
  */
 #ifndef PA_H
 #define PA_H
@@ -184,7 +191,11 @@ size_t pa_decode_partitioned_workspace_size(int num_seqs, int num_q_heads, int h
  * kernel is not launched.
  *
  *   max_context_len  an upper bound on every context_lens[s], known on the
- *                    host; it sizes the grid. A longer context gives NaN.
+ *                    host; it sizes the grid and the workspace. A context
+ *                    longer than ceil(max_context_len / partition_size) *
+ *                    partition_size tokens gives a NaN row (one a little
+ *                    over max_context_len but within that many partitions is
+ *                    still computed).
  *   partition_size   tokens per partition, a positive multiple of 16.
  *   workspace        device scratch of at least
  *                    pa_decode_partitioned_workspace_size(...) bytes, 256-byte
@@ -249,7 +260,9 @@ size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_
  *                      row, as does a prefix id outside [0, NB) (for every
  *                      sequence) or a suffix id outside [0, NB).
  *   max_context_len    an upper bound on every context_lens[s]; it sizes the
- *                      suffix partitions. A longer context gives NaN.
+ *                      suffix partitions. A context whose suffix (tokens past
+ *                      the prefix) is longer than NPs * partition_size
+ *                      tokens (NPs below) gives a NaN row.
  *   partition_size     suffix tokens per partition, a positive multiple of 16.
  *   num_blocks         NB >= 1 (PA_EINVAL for an empty pool).
  *   workspace          device scratch of at least

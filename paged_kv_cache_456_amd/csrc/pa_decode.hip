@@ -773,26 +773,24 @@ hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, int grid_partiti
     // Persistent: as many workgroups as the GPU keeps resident at once (never
     // more than there can be items).
     const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, waves) + persistent_lds_bytes(num_seqs);
-    int dev = 0, cus = 0, per_cu = 0, max_lds = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess)
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    int dev = 0, per_cu = 0;
+    DeviceInfo info{};
+    hipError_t e = current_device_info(&dev, &info);
     if (e != hipSuccess)
         return e;
-    if (lds > static_cast<size_t>(max_lds)) {
+    if (lds > static_cast<size_t>(info.max_lds)) {
         // The sequence list does not fit one workgroup's LDS: one workgroup
         // per (KV head, sequence, partition) computes the same partials.
         DecodeParams g = p;
         g.persistent = 0;
         return launch_decode_grid<KV, D, GMAX, OUT>(g, num_seqs, grid_partitions, waves, stream);
     }
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, waves * kWave, lds);
+    e = resident_workgroups_per_cu(dev, reinterpret_cast<const void*>(kernel), waves * kWave, lds,
+                                   &per_cu);
     if (e != hipSuccess)
         return e;
     const int64_t bound = static_cast<int64_t>(num_seqs) * p.num_kv_heads * grid_partitions;
-    const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(bound, static_cast<int64_t>(cus) *
+    const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(bound, static_cast<int64_t>(info.cus) *
                                                                          std::max(per_cu, 1)));
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(waves * kWave), lds, stream, p);
     return hipGetLastError();

@@ -176,6 +176,17 @@ struct CopyParams {
     int64_t block_bytes;           // Hkv * 16 * D * element bytes
 };
 
+// Facts of the current device, queried once per device (pa_device_cache.cpp).
+struct DeviceInfo {
+    int cus;         // compute units
+    int max_lds;     // LDS bytes one workgroup may use
+};
+hipError_t current_device_info(int* device, DeviceInfo* info);
+// Workgroups of `kernel` (`threads` threads, `lds` bytes of dynamic LDS) that
+// one compute unit of `device` keeps resident, queried once per combination.
+hipError_t resident_workgroups_per_cu(int device, const void* kernel, int threads, size_t lds,
+                                      int* per_cu);
+
 // Launchers (pa_decode.hip, pa_cache.hip). kv: 0 = fp32, 1 = bf16.
 hipError_t launch_decode(const DecodeParams& p, int kv_bf16, int head_size, int out_bf16,
                          int num_seqs, int grid_partitions, int waves, hipStream_t stream);

@@ -44,9 +44,11 @@ def test_tiny_fp32():
 @pytest.mark.parametrize("name,psizes,seqs", [
     ("llama8b_gqa_bf16", (None, 256, 512), None),
     ("prefix_shared_bf16", (None, 512), None),
-    ("long_context_bf16", (512,), [0, 5]),
+    ("long_context_bf16", (512, 1024), None),
 ])
 def test_workload(name, psizes, seqs):
+    """Every output row of the batch against the oracle (for the long-context batch: all 8
+    sequences of 32768 tokens, at the prescribed 512-token partitions and at 1024)."""
     w = wl.make_workload(name, device="cuda")
     r = oracle_step(w, seqs=seqs)
     idx = torch.as_tensor(r.seqs, device="cuda")
@@ -57,20 +59,46 @@ def test_workload(name, psizes, seqs):
         assert torch.isfinite(g.out).all()
 
 
+def large_batch_rows(w, count=40):
+    """Rows of the large batch the oracle checks: the longest and the shortest context, a
+    context whose table reaches a block at a byte offset of at least 2**32 in the pools,
+    and evenly spread others, `count` in all."""
+    L = w.context_lens.astype(np.int64)
+    nblk = -(-L // 16)
+    block_bytes = w.key_cache[0].numel() * w.key_cache.element_size()
+    far = [s for s in range(w.num_seqs)
+           if int(w.block_tables[s, :nblk[s]].max()) * block_bytes >= 2 ** 32]
+    assert far, "no context reaches past 4 GiB of the pool"
+    rows = {int(np.argmax(L)), int(np.argmin(L)), far[len(far) // 2]}
+    for s in np.linspace(0, w.num_seqs - 1, count).astype(int):
+        if len(rows) >= count:
+            break
+        rows.add(int(s))
+    return sorted(rows), block_bytes
+
+
 @pytest.mark.big
 def test_large_batch_sampled():
-    """256 sequences, pool of ~60% of HBM; the oracle checks a sample of sequences."""
+    """256 sequences, pool of ~60% of HBM; the oracle checks 40 of the 256 rows, among
+    them the longest and shortest contexts and one that reads a block past 4 GiB (64-bit
+    offsets); every other row must be finite."""
     free, _ = torch.cuda.mem_get_info()
     spec = wl.SPECS["large_batch_bf16"]
     per_block = 2 * spec.num_kv_heads * 16 * spec.head_size * 2
     nb = int(min(0.6 * wl.HBM_BYTES, 0.85 * free) // per_block)
     w = wl.make_workload("large_batch_bf16", device="cuda", poison=False, num_blocks=nb)
-    seqs = [0, 77, 254]
+    seqs, block_bytes = large_batch_rows(w)
+    assert len(seqs) >= 32
+    far = max(int(w.block_tables[s, :-(-int(w.context_lens[s]) // 16)].max()) for s in seqs)
+    print(f"large batch: {len(seqs)} rows checked, farthest block at byte {far * block_bytes}",
+          flush=True)
+    assert far * block_bytes >= 2 ** 32
     r = oracle_step(w, seqs=seqs, partition_size=512)
     g = gpu_step(w, partition_size=512, in_place=True)
     check_scatter(w, g, r, full_pool=False)
     _report("large_batch P=512", max_abs_err(g.out[torch.as_tensor(seqs, device="cuda")], r.out),
             TOL[torch.bfloat16])
+    assert torch.isfinite(g.out).all()
 
 
 # ---------------------------------------------------------------- shapes
