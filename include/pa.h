@@ -217,6 +217,40 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_partitioned_noalloc -- pa_decode_partitioned for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, and harnesses that forbid hipMalloc.
+ *
+ * Same arguments and result as pa_decode_partitioned, without the workspace
+ * arguments: the split's partials live in a buffer of
+ * PA_NOALLOC_WORKSPACE_BYTES that the library holds in device memory, one per
+ * GPU it runs on, from the first call on that GPU until the process ends.
+ * The call allocates and frees nothing (no hipMalloc, no allocating library
+ * routine) and, like every call here, only enqueues work on `stream`.
+ *
+ *   PA_EWORKSPACE  pa_decode_partitioned_workspace_size(num_seqs, num_q_heads,
+ *                  head_size, max_context_len, partition_size) exceeds
+ *                  PA_NOALLOC_WORKSPACE_BYTES (nothing is enqueued).
+ *   PA_EHIP        the buffer's device address could not be obtained.
+ *   Other checks and status codes are those of pa_decode_partitioned.
+ *
+ * Every call on one GPU uses that GPU's single buffer: two calls whose work
+ * may overlap in time on the same GPU (different streams, or host threads
+ * without ordering) race on it and give undefined results. Calls ordered on
+ * one stream are safe. The buffer keeps the last call's partials; nothing in
+ * it needs to start at zero.
+ */
+#define PA_NOALLOC_WORKSPACE_BYTES (64u * 1024u * 1024u)
+pa_status_t pa_decode_partitioned_noalloc(void* out, pa_dtype_t out_dtype, const void* query,
+                                          const void* key_cache, const void* value_cache,
+                                          pa_dtype_t kv_dtype, const int32_t* block_tables,
+                                          int max_blocks_per_seq, const int32_t* context_lens,
+                                          int num_seqs, int num_q_heads, int num_kv_heads,
+                                          int head_size, int block_size, int64_t num_blocks,
+                                          float scale, int max_context_len, int partition_size,
+                                          void* stream);
+
+/*
  * Workspace bytes pa_decode_cascade needs. With
  *   NPs = max(1, ceil(max(max_context_len - 16 * num_prefix_blocks, 0) / partition_size))
  *   NC  = ceil(num_prefix_blocks / 16),  NP = NPs + NC,  R = S * Hq * NP,

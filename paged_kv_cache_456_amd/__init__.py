@@ -7,6 +7,8 @@ declared in ``include/pa.h``). This package is its thin Python binding:
     pa_copy_blocks         copy whole blocks (copy-on-write)
     pa_decode              single-pass paged decode attention
     pa_decode_partitioned  split-context decode with a log-sum-exp reduce
+    pa_decode_partitioned_noalloc  the same with the library's own per-GPU
+                           workspace, for callers that cannot allocate
     pa_decode_cascade      decode over a prefix that every sequence shares,
                            read once per KV head, plus per-sequence suffixes
     pa_prefill             multi-token queries (a prompt or a chunk of one)
@@ -18,6 +20,7 @@ declared in ``include/pa.h``). This package is its thin Python binding:
 from ._lib import (  # noqa: F401
     PA_BF16, PA_F32, BlockManager, NoSpace, PagedAttentionError, cascade_workspace, decode_workspace, load,
     pa_copy_blocks, pa_decode, pa_decode_cascade, pa_decode_cascade_workspace_size,
-    pa_decode_partitioned, pa_decode_partitioned_workspace_size, pa_prefill, pa_reshape_and_cache,
+    pa_decode_partitioned, pa_decode_partitioned_noalloc, pa_decode_partitioned_workspace_size,
+    pa_prefill, pa_reshape_and_cache,
     pa_status_str, pa_stream_read, workspace_partials,
 )

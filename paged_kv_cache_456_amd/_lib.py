@@ -18,7 +18,8 @@ PA_F32, PA_BF16 = 0, 1
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOSPACE = 0, 1, 2, 3, 4, 5
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_partitioned",
-           "pa_decode_partitioned_workspace_size", "pa_decode_cascade",
+           "pa_decode_partitioned_workspace_size", "pa_decode_partitioned_noalloc",
+           "pa_decode_cascade",
            "pa_decode_cascade_workspace_size", "pa_prefill", "pa_stream_read", "pa_status_str",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token",
            "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_num_free_blocks", "pa_bm_length",
@@ -56,6 +57,9 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_partitioned.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32,
                                           i32, i64, f32, i32, i32, vp, sz, vp]
     lib.pa_decode_partitioned.restype = i32
+    lib.pa_decode_partitioned_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32,
+                                                  i32, i32, i32, i64, f32, i32, i32, vp]
+    lib.pa_decode_partitioned_noalloc.restype = i32
     lib.pa_decode_partitioned_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.pa_decode_partitioned_workspace_size.restype = sz
     lib.pa_decode_cascade.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32,
@@ -262,6 +266,30 @@ def pa_decode_partitioned(out: torch.Tensor, query: torch.Tensor, key_cache: tor
                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                       _stream(query, stream))
     _check(rc, "pa_decode_partitioned")
+    return out
+
+
+NOALLOC_WORKSPACE_BYTES = 64 * 1024 * 1024     # PA_NOALLOC_WORKSPACE_BYTES
+
+
+def pa_decode_partitioned_noalloc(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                                  value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, scale: float, max_context_len: int,
+                                  partition_size: int,
+                                  stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """pa_decode_partitioned with its workspace in the library's own per-GPU device buffer
+    (NOALLOC_WORKSPACE_BYTES): nothing is allocated. Calls that may overlap in time on one
+    GPU race on that buffer."""
+    S, Hq, Hkv, D, B, NB, MB = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                              context_lens)
+    rc = load().pa_decode_partitioned_noalloc(out.data_ptr(), _dtype_code(out.dtype),
+                                              query.data_ptr(), key_cache.data_ptr(),
+                                              value_cache.data_ptr(), _dtype_code(key_cache.dtype),
+                                              block_tables.data_ptr(), MB, context_lens.data_ptr(),
+                                              S, Hq, Hkv, D, B, NB, float(scale),
+                                              int(max_context_len), int(partition_size),
+                                              _stream(query, stream))
+    _check(rc, "pa_decode_partitioned_noalloc")
     return out
 
 

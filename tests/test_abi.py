@@ -135,6 +135,33 @@ def test_partitioned_checks(lib, kw, expect):
     assert part_call(lib, **kw) == expect
 
 
+def noalloc_call(lib, max_ctx=37, psize=32, **kw):
+    a = decode_args(**kw)
+    return lib.pa_decode_partitioned_noalloc(a["out"], a["out_dt"], a["q"], a["kc"], a["vc"],
+                                             a["kv_dt"], a["bt"], a["MB"], a["cl"], a["S"], a["Hq"],
+                                             a["Hkv"], a["D"], a["B"], a["NB"], a["scale"], max_ctx,
+                                             psize, None)
+
+
+@pytest.mark.parametrize("kw,expect", DECODE_CASES)
+def test_noalloc_shares_decode_checks(lib, kw, expect):
+    """The no-allocation variant runs every host check of the partitioned call before it
+    looks up its device buffer (so none of these touches a GPU)."""
+    if expect == OK and kw.get("S", 1) != 0:
+        pytest.skip("would launch")
+    assert noalloc_call(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(psize=24), EINVAL), (dict(psize=0), EINVAL), (dict(max_ctx=-1), EINVAL),
+    (dict(max_ctx=16 * 70000, psize=16), EUNSUP), (dict(S=0), OK),
+    # partials beyond the library's buffer: refused before anything else happens
+    (dict(S=256, Hq=64, Hkv=8, D=128, max_ctx=8192, psize=16), EWS),
+])
+def test_noalloc_checks(lib, kw, expect):
+    assert noalloc_call(lib, **kw) == expect
+
+
 def test_workspace_size_formula(lib):
     a256 = lambda n: (n + 255) // 256 * 256
     for S, Hq, D, L, Ps in [(64, 32, 128, 4096, 256), (8, 64, 128, 32768, 512), (4, 4, 64, 37, 32),
