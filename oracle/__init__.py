@@ -1,6 +1,7 @@
 """fp64 CPU oracle for paged decode attention, multi-token queries over the paged
-cache, the KV-cache write and the copy-on-write block copy (the block manager's
-reference model is the plain Python of ``block_manager.py``).
+cache, the KV-cache write, the copy-on-write block copy and the block swap between
+two pools (the block manager's reference model is the plain Python of
+``block_manager.py``).
 
 TEST INFRASTRUCTURE ONLY. The test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` are the only callers. The GPU library never
@@ -79,6 +80,9 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.oracle_copy_blocks.argtypes = [u8p, u8p, i64p, ctypes.c_int64, ctypes.c_int64,
                                         ctypes.c_int64]
     lib.oracle_copy_blocks.restype = ctypes.c_int
+    lib.oracle_swap_blocks.argtypes = [u8p, u8p, ctypes.c_int64, u8p, u8p, ctypes.c_int64, i64p,
+                                       ctypes.c_int64, ctypes.c_int64]
+    lib.oracle_swap_blocks.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -169,6 +173,29 @@ def copy_blocks(key_cache: np.ndarray, value_cache: np.ndarray, block_mapping,
     block_bytes = key_cache.nbytes // NB if NB else 1
     rc = lib.oracle_copy_blocks(key_cache.ctypes.data, value_cache.ctypes.data,
                                 _ptr(pairs, ctypes.c_int64), pairs.shape[0], block_bytes, NB)
+    _check(rc)
+
+
+def swap_blocks(src_key: np.ndarray, src_value: np.ndarray, dst_key: np.ndarray,
+                dst_value: np.ndarray, block_mapping, lib: Optional[ctypes.CDLL] = None) -> None:
+    """Block swap between two pairs of pools, byte for byte: for each pair (src, dst) of
+    block_mapping ([N, 2] int64), block dst of the destination pools becomes a copy of
+    block src of the source pools (both K and V). Pools are [NB, Hkv, B, D] numpy arrays
+    (bf16 as uint16 views), C-contiguous; source and destination may differ in NB only.
+    The destination arrays are written in place."""
+    lib = lib or _lib()
+    for a in (src_key, src_value, dst_key, dst_value):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("arrays must be C-contiguous")
+    if src_key.shape != src_value.shape or dst_key.shape != dst_value.shape or \
+            src_key.shape[1:] != dst_key.shape[1:] or \
+            len({src_key.dtype, src_value.dtype, dst_key.dtype, dst_value.dtype}) != 1:
+        raise ValueError("pools must share a block shape and dtype")
+    pairs = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2))
+    block_bytes = int(np.prod(src_key.shape[1:])) * src_key.itemsize
+    rc = lib.oracle_swap_blocks(src_key.ctypes.data, src_value.ctypes.data, src_key.shape[0],
+                                dst_key.ctypes.data, dst_value.ctypes.data, dst_key.shape[0],
+                                _ptr(pairs, ctypes.c_int64), pairs.shape[0], block_bytes)
     _check(rc)
 
 

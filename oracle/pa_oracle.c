@@ -1,7 +1,7 @@
 /*
  * pa_oracle.c -- plain fp64 CPU oracle for paged KV-cache decode attention,
- * multi-token queries over the paged cache, the KV-cache write and the
- * copy-on-write block copy.
+ * multi-token queries over the paged cache, the KV-cache write, the
+ * copy-on-write block copy and the swap of blocks between two pools.
  *
  * TEST INFRASTRUCTURE ONLY. The test suite, the package smoke check and the
  * CPU-baseline leg of the benchmark are the only code that may load this
@@ -502,6 +502,45 @@ int oracle_copy_blocks(uint8_t* key_cache, uint8_t* value_cache, const int64_t* 
             continue;
         memcpy(key_cache + dst * block_bytes, key_cache + src * block_bytes, (size_t)block_bytes);
         memcpy(value_cache + dst * block_bytes, value_cache + src * block_bytes, (size_t)block_bytes);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Swap ("Why read its source at all" on "What vLLM Is and Why It Exists":
+ * preemption takes a request's blocks away to feed another; "Idea 1:
+ * PagedAttention", day-9 post: the cache lives in fixed-size blocks). A
+ * reading: a preempted request's blocks are moved out of the GPU pools into a
+ * second pair of pools (host memory) and later back, each block whole --
+ * every KV head, every row -- byte for byte. Each pair (src, dst) of
+ * block_mapping copies block src of the source pools onto block dst of the
+ * destination pools. A pair with a negative id is skipped; an id past its
+ * pool, or a destination named twice (the result would depend on the order),
+ * is an error and nothing is written. Source and destination pools are
+ * different memory.
+ */
+int oracle_swap_blocks(const uint8_t* src_key, const uint8_t* src_value, int64_t src_num_blocks,
+                       uint8_t* dst_key, uint8_t* dst_value, int64_t dst_num_blocks,
+                       const int64_t* block_mapping, int64_t num_pairs, int64_t block_bytes)
+{
+    if (num_pairs < 0 || block_bytes <= 0 || src_num_blocks < 0 || dst_num_blocks < 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        if (src < 0 || dst < 0)
+            continue;
+        if (src >= src_num_blocks || dst >= dst_num_blocks)
+            return ORACLE_BAD_PAIR;
+        for (int64_t j = i + 1; j < num_pairs; ++j)
+            if (block_mapping[2 * j] >= 0 && block_mapping[2 * j + 1] == dst)
+                return ORACLE_BAD_PAIR;
+    }
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        if (src < 0 || dst < 0)
+            continue;
+        memcpy(dst_key + dst * block_bytes, src_key + src * block_bytes, (size_t)block_bytes);
+        memcpy(dst_value + dst * block_bytes, src_value + src * block_bytes, (size_t)block_bytes);
     }
     return ORACLE_OK;
 }

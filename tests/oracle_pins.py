@@ -431,6 +431,75 @@ def pin_copy_blocks_rejects(lib):
         raise AssertionError(f"pairs {pairs} accepted")
 
 
+def pin_swap_blocks_positions(lib):
+    """Swap between two pairs of pools of different sizes: block dst of the destination
+    pools becomes block src of the source pools, K from K and V from V, bit for bit (NaN
+    payloads too); pairs with a negative id are skipped; the source pools and every other
+    destination block are unchanged."""
+    rng = np.random.default_rng(32)
+    Hkv, D = 2, 8
+    sk = rng.integers(0, 1 << 16, size=(7, Hkv, B, D), dtype=np.uint16)
+    sv = rng.integers(0, 1 << 16, size=(7, Hkv, B, D), dtype=np.uint16)
+    sk[3, 1, 15, 7] = 0x7FC3                      # a NaN payload travels as it is
+    dk = rng.integers(0, 1 << 16, size=(4, Hkv, B, D), dtype=np.uint16)
+    dv = rng.integers(0, 1 << 16, size=(4, Hkv, B, D), dtype=np.uint16)
+    sk0, sv0, dk0, dv0 = sk.copy(), sv.copy(), dk.copy(), dv.copy()
+    oracle.swap_blocks(sk, sv, dk, dv, [[3, 0], [6, 2], [-1, 1], [5, -3]], lib=lib)
+    assert np.array_equal(sk, sk0) and np.array_equal(sv, sv0)
+    assert np.array_equal(dk[0], sk0[3]) and np.array_equal(dv[0], sv0[3])
+    assert np.array_equal(dk[2], sk0[6]) and np.array_equal(dv[2], sv0[6])
+    assert np.array_equal(dk[[1, 3]], dk0[[1, 3]]) and np.array_equal(dv[[1, 3]], dv0[[1, 3]])
+    assert dk[0, 1, 15, 7] == 0x7FC3
+
+
+def pin_swap_round_trip_decode(lib):
+    """Preemption by swapping: a sequence's blocks moved out to a second pool and back
+    into different physical blocks of the first, with its table remapped, give the same
+    decode output bit for bit (blocks can sit anywhere: day-9 post, "Why this wins"), and
+    the blocks hold exactly their old bytes."""
+    rng = np.random.default_rng(33)
+    p = random_problem(rng, [37, 20], 8, 2, 16)
+    ref = run(lib, p)
+    kc, vc = p["kc"], p["vc"]
+    NB = kc.shape[0]
+    bt = p["bt"].copy()
+    nblk = -(-int(p["cl"][0]) // B)
+    blocks = bt[0, :nblk].astype(np.int64)
+    hk = np.zeros((5,) + kc.shape[1:], kc.dtype)
+    hv = np.zeros_like(hk)
+    host_ids = np.array([4, 0, 2])[:nblk]
+    oracle.swap_blocks(kc, vc, hk, hv, np.stack([blocks, host_ids], 1), lib=lib)
+    kc2 = np.full((NB + 3,) + kc.shape[1:], np.nan, kc.dtype)
+    vc2 = np.full_like(kc2, np.nan)
+    kc2[:NB], vc2[:NB] = kc, vc
+    kc2[blocks], vc2[blocks] = np.nan, np.nan     # the old copies are gone
+    fresh = np.arange(NB, NB + nblk)
+    oracle.swap_blocks(hk, hv, kc2, vc2, np.stack([host_ids, fresh], 1), lib=lib)
+    bits = lambda a: a.view(np.uint64)            # tail rows hold NaN poison: compare bits
+    assert np.array_equal(bits(kc2[fresh]), bits(kc[blocks]))
+    assert np.array_equal(bits(vc2[fresh]), bits(vc[blocks]))
+    bt[0, :nblk] = fresh
+    out = run(lib, {**p, "kc": kc2, "vc": vc2, "bt": bt})
+    assert np.array_equal(out, ref)
+
+
+def pin_swap_blocks_rejects(lib):
+    """A destination named twice, or an id past its own pool, is an error; nothing is
+    written."""
+    rng = np.random.default_rng(34)
+    sk = rng.integers(0, 1 << 16, size=(3, 1, B, 4), dtype=np.uint16)
+    dk = rng.integers(0, 1 << 16, size=(5, 1, B, 4), dtype=np.uint16)
+    for pairs in ([[0, 1], [2, 1]], [[3, 0]], [[0, 5]], [[1, 2], [0, 7]]):
+        d0 = dk.copy()
+        try:
+            oracle.swap_blocks(sk, sk.copy(), dk, dk.copy(), pairs, lib=lib)
+        except oracle.OracleError:
+            assert np.array_equal(dk, d0)
+            continue
+        raise AssertionError(f"pairs {pairs} accepted")
+    oracle.swap_blocks(sk, sk.copy(), dk, dk.copy(), [[2, 4], [0, 0]], lib=lib)  # in range: fine
+
+
 # --------------------------------------------------------------------------
 # Multi-token queries (a prompt chunk per sequence) over the paged cache
 # --------------------------------------------------------------------------

@@ -16,6 +16,12 @@ MUTANTS = [
      "memcpy(key_cache + src * block_bytes, key_cache + dst * block_bytes,", 1),
     ("copy_v_from_k", "memcpy(value_cache + dst * block_bytes, value_cache + src * block_bytes,",
      "memcpy(value_cache + dst * block_bytes, key_cache + src * block_bytes,", 1),
+    ("swap_half_block", "memcpy(dst_key + dst * block_bytes, src_key + src * block_bytes, (size_t)block_bytes);",
+     "memcpy(dst_key + dst * block_bytes, src_key + src * block_bytes, (size_t)block_bytes / 2);", 1),
+    ("swap_v_from_k", "memcpy(dst_value + dst * block_bytes, src_value + src * block_bytes,",
+     "memcpy(dst_value + dst * block_bytes, src_key + src * block_bytes,", 1),
+    ("swap_skips_first_pair", "for (int64_t i = 0; i < num_pairs; ++i) {\n        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];\n        if (src < 0 || dst < 0)\n            continue;\n        memcpy(dst_key",
+     "for (int64_t i = 1; i < num_pairs; ++i) {\n        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];\n        if (src < 0 || dst < 0)\n            continue;\n        memcpy(dst_key", 1),
     ("gqa_interleaved", "const int h = kv * group + g;", "const int h = g * num_kv_heads + kv;", 2),
     ("scale_dropped", "l[t] = scale * dot;", "l[t] = dot;", 1),
     ("exp_sign", "l[t] = exp(l[t] - m);", "l[t] = exp(m - l[t]);", 1),
