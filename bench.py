@@ -74,8 +74,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--op", choices=("decode", "copy_blocks", "prefill"), default="decode",
+    ap.add_argument("--op", choices=("decode", "copy_blocks", "swap", "prefill"), default="decode",
                     help="decode: the decode step (default); copy_blocks: pa_copy_blocks alone; "
+                         "swap: pa_swap_blocks out to pinned host pools and back; "
                          "prefill: pa_prefill, a chunk of query tokens per sequence")
     ap.add_argument("--prefill-chunk", type=int, default=512,
                     help="--op prefill: query tokens per sequence (its last min(L, chunk) tokens)")
@@ -117,6 +118,8 @@ def main() -> int:
         return bench_copy_blocks(args, dev)
     if args.op == "prefill":
         return bench_prefill(args, dev)
+    if args.op == "swap":
+        return bench_swap(args, dev)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -341,6 +344,73 @@ def bench_copy_blocks(args, dev) -> int:
                      "kernel": "copy_blocks_kernel",
                      "timing": "HIP events around the timed calls, mean per call"},
         "cow_128_pairs_us": round(small_s * 1e6, 3),
+        "cpu_baseline": None,
+    }), flush=True)
+    return 0
+
+
+PCIE5_X16_GBS = 64.0     # the GPU's host link, PCIe 5.0 x16, nominal per direction
+
+
+def bench_swap(args, dev) -> int:
+    """pa_swap_blocks on the Llama-8B pool shapes (8 KV heads, D = 128, bf16: 32 KB per block
+    per pool): 1024 scattered blocks of a 16384-block GPU pool swapped out to pinned host
+    pools (64 MB over the host link per call), then back into other GPU blocks. Synthetic
+    data. The bound is the host link, not HBM."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_456_amd as pa
+
+    Hkv, D, NB, HNB, npairs = 8, 128, 16384, 2048, 1024
+    block_bytes = Hkv * 16 * D * 2
+    kc = torch.empty((NB, Hkv, 16, D), dtype=torch.bfloat16, device=dev).normal_()
+    vc = torch.empty_like(kc).normal_()
+    hk = torch.zeros((HNB, Hkv, 16, D), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    rng = np.random.default_rng(6)
+    outs, ins = [], []
+    for _ in range(4):
+        dblk = rng.permutation(NB)[:npairs]
+        hblk = rng.permutation(HNB)[:npairs]
+        outs.append(torch.from_numpy(np.stack([dblk, hblk], 1)).to(dev))
+        ins.append(torch.from_numpy(np.stack([hblk, rng.permutation(NB)[:npairs]], 1)).to(dev))
+
+    def timed(fn, steps):
+        for i in range(min(args.warmup, 10)):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / steps
+
+    steps = min(args.steps, 50)
+    t_out = timed(lambda i: pa.pa_swap_blocks(kc, vc, hk, hv, outs[i % 4]), steps)
+    t_in = timed(lambda i: pa.pa_swap_blocks(hk, hv, kc, vc, ins[i % 4]), steps)
+    moved = 2 * npairs * block_bytes                  # both pools, one direction
+    gbs_out, gbs_in = moved / t_out / 1e9, moved / t_in / 1e9
+    log(f"[bench] swap {npairs} blocks ({moved / 1e6:.1f} MB): out {t_out * 1e6:.1f} us "
+        f"({gbs_out:.1f} GB/s), in {t_in * 1e6:.1f} us ({gbs_in:.1f} GB/s)")
+    print(json.dumps({
+        "metric": "block swap GB/s between GPU pools and pinned host pools (bytes moved, mean "
+                  "of the two directions)",
+        "value": round((gbs_out + gbs_in) / 2, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": min(args.warmup, 10), "ms_per_step": round((t_out + t_in) * 1e3 / 2, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "swap_blocks", "num_pairs": npairs, "num_kv_heads": Hkv,
+                   "head_size": D, "block_bytes_per_pool": block_bytes, "pool_blocks": NB,
+                   "host_pool_blocks": HNB},
+        "swap_out_gbs": round(gbs_out, 2), "swap_in_gbs": round(gbs_in, 2),
+        "roofline": {"bound": "host link", "achieved": round((gbs_out + gbs_in) / 2, 2),
+                     "peak": PCIE5_X16_GBS, "unit": "GB/s",
+                     "frac": round((gbs_out + gbs_in) / 2 / PCIE5_X16_GBS, 4), "traffic": None,
+                     "kernel": "swap_blocks_kernel",
+                     "timing": "HIP events around the timed calls, mean per call"},
         "cpu_baseline": None,
     }), flush=True)
     return 0

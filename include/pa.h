@@ -10,6 +10,8 @@
  *
  *   pa_reshape_and_cache   write each new token's key and value into its slot
  *   pa_copy_blocks         copy whole blocks (copy-on-write of a shared block)
+ *   pa_swap_blocks         move whole blocks between the GPU pools and host
+ *                          pools (swap a preempted sequence out and back in)
  *   pa_decode              one query token per sequence attends over its
  *                          block-scattered context (single pass)
  *   pa_decode_partitioned  the same result, with each context cut into
@@ -139,6 +141,37 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value,
 pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
                            int64_t num_pairs, int num_kv_heads, int head_size, int block_size,
                            int64_t num_blocks, pa_dtype_t kv_dtype, void* stream);
+
+/*
+ * pa_swap_blocks -- move whole blocks between two pairs of pools, typically
+ * the GPU pools and a pair of pools in pinned host memory (swap out a
+ * preempted sequence, later swap it back in).
+ *
+ * "Preemption" takes a request's blocks away to feed another ("Why read its
+ * source at all" on "What vLLM Is and Why It Exists"); keeping those blocks'
+ * contents in host memory lets the request resume without recomputing them.
+ * For each pair i, block block_mapping[2i] of the source pools (every KV head,
+ * every row, K and V) is copied onto block block_mapping[2i + 1] of the
+ * destination pools, byte for byte. Swap-in after swap-out returns the same
+ * bytes, so a table remapped to the new blocks decodes bit-identically.
+ *
+ *   src_key_cache, src_value_cache  [src_num_blocks][Hkv][16][D] of kv_dtype
+ *   dst_key_cache, dst_value_cache  [dst_num_blocks][Hkv][16][D], written
+ *   block_mapping  int64 [num_pairs][2] (source id, destination id). A pair
+ *                  with a negative id, or an id past its own pool, is
+ *                  skipped. Destination ids must be distinct.
+ * Every pointer is memory the GPU can address: device memory, or pinned host
+ * memory (hipHostMalloc; torch's pin_memory()), which the kernel reads or
+ * writes across the host link. Pageable host memory gives PA_EINVAL. Source
+ * and destination pools must not overlap. The call is asynchronous on
+ * `stream`: host pools must stay allocated and untouched until it finishes.
+ * num_pairs = 0 is valid and enqueues nothing.
+ */
+pa_status_t pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                           int64_t src_num_blocks, void* dst_key_cache, void* dst_value_cache,
+                           int64_t dst_num_blocks, const int64_t* block_mapping, int64_t num_pairs,
+                           int num_kv_heads, int head_size, int block_size, pa_dtype_t kv_dtype,
+                           void* stream);
 
 /*
  * pa_decode -- single-pass paged decode attention.

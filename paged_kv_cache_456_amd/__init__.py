@@ -5,6 +5,7 @@ declared in ``include/pa.h``). This package is its thin Python binding:
 
     pa_reshape_and_cache   write new tokens' K/V into their cache slots
     pa_copy_blocks         copy whole blocks (copy-on-write)
+    pa_swap_blocks         move whole blocks between GPU pools and pinned host pools
     pa_decode              single-pass paged decode attention
     pa_decode_partitioned  split-context decode with a log-sum-exp reduce
     pa_decode_partitioned_noalloc  the same with the library's own per-GPU
@@ -22,5 +23,5 @@ from ._lib import (  # noqa: F401
     pa_copy_blocks, pa_decode, pa_decode_cascade, pa_decode_cascade_workspace_size,
     pa_decode_partitioned, pa_decode_partitioned_noalloc, pa_decode_partitioned_workspace_size,
     pa_prefill, pa_reshape_and_cache,
-    pa_status_str, pa_stream_read, workspace_partials,
+    pa_status_str, pa_stream_read, pa_swap_blocks, workspace_partials,
 )

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_F32, PA_BF16 = 0, 1
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOSPACE = 0, 1, 2, 3, 4, 5
 
-EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_partitioned",
+EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode", "pa_decode_partitioned",
            "pa_decode_partitioned_workspace_size", "pa_decode_partitioned_noalloc",
            "pa_decode_cascade",
            "pa_decode_cascade_workspace_size", "pa_prefill", "pa_stream_read", "pa_status_str",
@@ -49,6 +49,8 @@ def load() -> ctypes.CDLL:
     lib.pa_reshape_and_cache.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
     lib.pa_copy_blocks.restype = i32
+    lib.pa_swap_blocks.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, i32, i32, i32, i32, vp]
+    lib.pa_swap_blocks.restype = i32
     lib.pa_stream_read.argtypes = [vp, i64, vp, i32, vp]
     lib.pa_stream_read.restype = i32
     lib.pa_decode.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i64,
@@ -165,6 +167,38 @@ def pa_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
                                block_mapping.shape[0], Hkv, D, B, NB, _dtype_code(key_cache.dtype),
                                _stream(key_cache, stream))
     _check(rc, "pa_copy_blocks")
+
+
+def pa_swap_blocks(src_key: torch.Tensor, src_value: torch.Tensor, dst_key: torch.Tensor,
+                   dst_value: torch.Tensor, block_mapping: torch.Tensor,
+                   stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Copy block block_mapping[i, 0] of the source pools onto block block_mapping[i, 1] of
+    the destination pools (K and V), asynchronously. Each tensor is a GPU tensor or a
+    pinned host tensor (torch pin_memory()); block_mapping is int64 [N, 2]. The stream is
+    the current stream of the GPU that holds a GPU operand (or of the current GPU)."""
+    ts = (src_key, src_value, dst_key, dst_value, block_mapping)
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous tensors")
+        if t.device.type != "cuda" and not t.is_pinned():
+            raise ValueError("host tensors must be pinned (pin_memory()): the GPU reads them")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise TypeError("block_mapping must be int64 [N, 2]")
+    SNB, Hkv, B, D = src_key.shape
+    DNB = dst_key.shape[0]
+    if src_value.shape != src_key.shape or dst_value.shape != dst_key.shape or \
+            dst_key.shape[1:] != src_key.shape[1:]:
+        raise ValueError("pools must share their block shape")
+    if len({src_key.dtype, src_value.dtype, dst_key.dtype, dst_value.dtype}) != 1:
+        raise TypeError("pools must share one dtype")
+    gpu = next((t.device for t in ts if t.device.type == "cuda"), None)
+    if stream is None:
+        stream = torch.cuda.current_stream(gpu)
+    rc = load().pa_swap_blocks(src_key.data_ptr(), src_value.data_ptr(), SNB, dst_key.data_ptr(),
+                               dst_value.data_ptr(), DNB, block_mapping.data_ptr(),
+                               block_mapping.shape[0], Hkv, D, B, _dtype_code(src_key.dtype),
+                               stream.cuda_stream)
+    _check(rc, "pa_swap_blocks")
 
 
 def pa_stream_read(src: torch.Tensor, sink: torch.Tensor,

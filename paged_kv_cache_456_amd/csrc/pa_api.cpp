@@ -190,6 +190,67 @@ pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* bl
     return from_hip(pa::launch_copy_blocks(p, num_pairs, static_cast<hipStream_t>(stream)));
 }
 
+// The address a kernel uses for `p`: device memory as it is, pinned host
+// memory (hipHostMalloc, torch's pin_memory) through its device mapping.
+// Anything else (pageable host memory) is refused: the GPU cannot read it.
+static bool device_address(const void* p, const void** out) {
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();                  // clear the runtime's error state
+        return false;
+    }
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+        *out = p;
+        return true;
+    }
+    if (a.type == hipMemoryTypeHost && a.devicePointer != nullptr) {
+        const char* base = static_cast<const char*>(a.hostPointer ? a.hostPointer : p);
+        *out = static_cast<const char*>(a.devicePointer) + (static_cast<const char*>(p) - base);
+        return true;
+    }
+    return false;
+}
+
+pa_status_t pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                           int64_t src_num_blocks, void* dst_key_cache, void* dst_value_cache,
+                           int64_t dst_num_blocks, const int64_t* block_mapping, int64_t num_pairs,
+                           int num_kv_heads, int head_size, int block_size, pa_dtype_t kv_dtype,
+                           void* stream) {
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 ||
+        src_num_blocks < 0 || dst_num_blocks < 0)
+        return PA_EINVAL;
+    if (!dtype_ok(kv_dtype) || block_size != pa::kBlockSize || (head_size != 64 && head_size != 128))
+        return PA_EUNSUPPORTED;
+    if (num_pairs > INT32_MAX)
+        return PA_EUNSUPPORTED;
+    if (num_pairs == 0)
+        return PA_OK;
+    if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache || !block_mapping)
+        return PA_EINVAL;
+    if (!aligned(src_key_cache, 16) || !aligned(src_value_cache, 16) || !aligned(dst_key_cache, 16) ||
+        !aligned(dst_value_cache, 16) || !aligned(block_mapping, 8))
+        return PA_EINVAL;
+    const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * pa::kBlockSize * head_size *
+                                elem_bytes(kv_dtype);
+    if (src_num_blocks > INT64_MAX / block_bytes || dst_num_blocks > INT64_MAX / block_bytes)
+        return PA_EINVAL;
+    const void *sk, *sv, *dk, *dv, *map;
+    if (!device_address(src_key_cache, &sk) || !device_address(src_value_cache, &sv) ||
+        !device_address(dst_key_cache, &dk) || !device_address(dst_value_cache, &dv) ||
+        !device_address(block_mapping, &map))
+        return PA_EINVAL;
+    pa::SwapParams p{};
+    p.src_key = static_cast<const uint8_t*>(sk);
+    p.src_value = static_cast<const uint8_t*>(sv);
+    p.dst_key = static_cast<uint8_t*>(const_cast<void*>(dk));
+    p.dst_value = static_cast<uint8_t*>(const_cast<void*>(dv));
+    p.block_mapping = static_cast<const int64_t*>(map);
+    p.src_num_blocks = src_num_blocks;
+    p.dst_num_blocks = dst_num_blocks;
+    p.block_bytes = block_bytes;
+    return from_hip(pa::launch_swap_blocks(p, num_pairs, static_cast<hipStream_t>(stream)));
+}
+
 pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* query, const void* key_cache,
                       const void* value_cache, pa_dtype_t kv_dtype, const int32_t* block_tables,
                       int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,

@@ -51,16 +51,11 @@ __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(CacheP
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 8;
 
-__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyParams p) {
-    const int64_t i = blockIdx.x;
-    const int64_t src = p.block_mapping[2 * i];
-    const int64_t dst = p.block_mapping[2 * i + 1];
-    if (src < 0 || dst < 0 || src >= p.num_blocks || dst >= p.num_blocks)
-        return;                                    // skipped pair, or an id outside the pool
-    uint8_t* pool = blockIdx.y ? p.value_cache : p.key_cache;
-    const u32x4* from = reinterpret_cast<const u32x4*>(pool + src * p.block_bytes);
-    u32x4* to = reinterpret_cast<u32x4*>(pool + dst * p.block_bytes);
-    const int64_t n = p.block_bytes / 16;
+// One block of one pool, `block_bytes` bytes, copied by the workgroup.
+__device__ __forceinline__ void copy_block(const uint8_t* src, uint8_t* dst, int64_t block_bytes) {
+    const u32x4* from = reinterpret_cast<const u32x4*>(src);
+    u32x4* to = reinterpret_cast<u32x4*>(dst);
+    const int64_t n = block_bytes / 16;
     for (int64_t c0 = threadIdx.x; c0 < n; c0 += static_cast<int64_t>(blockDim.x) * kCopyUnroll) {
         u32x4 v[kCopyUnroll];
 #pragma unroll
@@ -78,10 +73,43 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyParams p)
     }
 }
 
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyParams p) {
+    const int64_t i = blockIdx.x;
+    const int64_t src = p.block_mapping[2 * i];
+    const int64_t dst = p.block_mapping[2 * i + 1];
+    if (src < 0 || dst < 0 || src >= p.num_blocks || dst >= p.num_blocks)
+        return;                                    // skipped pair, or an id outside the pool
+    uint8_t* pool = blockIdx.y ? p.value_cache : p.key_cache;
+    copy_block(pool + src * p.block_bytes, pool + dst * p.block_bytes, p.block_bytes);
+}
+
+// Swap of whole blocks between two pairs of pools (preemption moves a
+// request's blocks out of the GPU pools and back: "Why read its source at
+// all" on "What vLLM Is and Why It Exists"). Pair i copies block src of the
+// source pools onto block dst of the destination pools; one side is usually
+// pinned host memory, read or written by the kernel across the host link.
+// Grid: (pairs, 2 pools), as the copy above.
+__global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(SwapParams p) {
+    const int64_t i = blockIdx.x;
+    const int64_t src = p.block_mapping[2 * i];
+    const int64_t dst = p.block_mapping[2 * i + 1];
+    if (src < 0 || dst < 0 || src >= p.src_num_blocks || dst >= p.dst_num_blocks)
+        return;                                    // skipped pair, or an id outside its pool
+    const uint8_t* from = blockIdx.y ? p.src_value : p.src_key;
+    uint8_t* to = blockIdx.y ? p.dst_value : p.dst_key;
+    copy_block(from + src * p.block_bytes, to + dst * p.block_bytes, p.block_bytes);
+}
+
 }  // namespace
 
 hipError_t launch_copy_blocks(const CopyParams& p, int64_t num_pairs, hipStream_t stream) {
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(num_pairs), 2),
+                       dim3(kCopyThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const SwapParams& p, int64_t num_pairs, hipStream_t stream) {
+    hipLaunchKernelGGL(swap_blocks_kernel, dim3(static_cast<unsigned>(num_pairs), 2),
                        dim3(kCopyThreads), 0, stream, p);
     return hipGetLastError();
 }

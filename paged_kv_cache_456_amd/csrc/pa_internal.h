@@ -176,6 +176,17 @@ struct CopyParams {
     int64_t block_bytes;           // Hkv * 16 * D * element bytes
 };
 
+struct SwapParams {
+    const uint8_t* src_key;        // source pools [src_num_blocks][Hkv][16][D]
+    const uint8_t* src_value;
+    uint8_t* dst_key;              // destination pools [dst_num_blocks][Hkv][16][D]
+    uint8_t* dst_value;
+    const int64_t* block_mapping;  // [N][2]: source block, destination block
+    int64_t src_num_blocks;
+    int64_t dst_num_blocks;
+    int64_t block_bytes;           // Hkv * 16 * D * element bytes
+};
+
 // Facts of the current device, queried once per device (pa_device_cache.cpp).
 struct DeviceInfo {
     int cus;         // compute units
@@ -194,6 +205,7 @@ hipError_t launch_reduce(const ReduceParams& p, int head_size, int out_bf16, int
                          hipStream_t stream);
 hipError_t launch_cache(const CacheParams& p, int64_t num_tokens, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, int64_t num_pairs, hipStream_t stream);
+hipError_t launch_swap_blocks(const SwapParams& p, int64_t num_pairs, hipStream_t stream);
 hipError_t launch_cascade_prefix(const CascadeParams& p, int head_size, int num_chunks,
                                  hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_size, int out_bf16, int num_seqs,

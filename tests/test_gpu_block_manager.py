@@ -4,7 +4,10 @@ Each step: requests arrive (prompt tokens written with pa_reshape_and_cache), so
 (sharing their blocks), some finish; then every running sequence appends one token. The
 library's block manager hands out the slots; a copy-on-write pair it reports is applied
 with pa_copy_blocks right away; when the pool is full the youngest sequence that has not
-stepped yet is preempted. The step's decode (pa_decode_partitioned and pa_decode over the
+stepped yet is preempted: its blocks are swapped out to pinned host pools with
+pa_swap_blocks (when the host pools have room, else it is dropped), and it is swapped back
+into fresh blocks at the start of a later step once the pool has room, where a probe
+decode of it alone must give the same bits as before it left. The step's decode (pa_decode_partitioned and pa_decode over the
 manager's tables) is compared with the fp64 oracle run on caches rebuilt from each
 sequence's own token history -- never from the GPU pool -- so a wrong slot, a missed or
 misdirected copy, or a stale table shows up as an error."""
@@ -21,6 +24,7 @@ pytestmark = pytest.mark.gpu
 B, HQ, HKV, D = 16, 8, 2, 64
 NB, MB = 48, 16
 MAX_ORIGINS, MAX_POS = 160, MB * B
+HOST_NB = 24                    # blocks of the pinned host pools that hold swapped-out sequences
 
 
 def test_continuous_batching_steps():
@@ -37,7 +41,51 @@ def test_continuous_batching_steps():
     hist = {}                  # sequence -> list of token tags (origin, position)
     order = []                 # running sequences, oldest first
     next_id = 0
-    stats = {"cow": 0, "preempt": 0, "fork": 0, "checked": 0}
+    stats = {"cow": 0, "preempt": 0, "fork": 0, "checked": 0, "swap_out": 0, "swap_in": 0}
+    host_k = torch.full((HOST_NB, HKV, B, D), float("nan"), dtype=torch.bfloat16).pin_memory()
+    host_v = torch.full_like(host_k, float("nan")).pin_memory()
+    host_free = list(range(HOST_NB))
+    swapped = {}               # sequence -> (host blocks, history, probe query, probe output)
+
+    def probe(s_table, n, qp):
+        """Decode of one sequence alone (single pass) with a fixed probe query."""
+        bt1 = torch.tensor([s_table + [-1] * (MB - len(s_table))], dtype=torch.int32, device=dev)
+        o = torch.empty((1, HQ, D), dtype=torch.float32, device=dev)
+        pa.pa_decode(o, qp, kc, vc, bt1, torch.tensor([n], dtype=torch.int32, device=dev), scale)
+        return o
+
+    def swap_out(v):
+        n = len(hist[v])
+        table = bm.table(v)
+        if len(table) > len(host_free):
+            return False
+        qp = torch.randn((1, HQ, D), generator=gen).to(torch.bfloat16).to(dev)
+        before = probe(table, n, qp)
+        hb = [host_free.pop() for _ in table]
+        pa.pa_swap_blocks(kc, vc, host_k, host_v,
+                          torch.tensor(list(zip(table, hb)), dtype=torch.int64, device=dev))
+        swapped[v] = (hb, hist[v], qp, before)
+        stats["swap_out"] += 1
+        return True
+
+    def swap_in(v):
+        hb, h, qp, before = swapped[v]
+        try:
+            slots = bm.add_sequence(v, len(h))      # fresh blocks for every token
+        except pa.NoSpace:
+            return False
+        table = [int(slots[j * B]) // B for j in range(len(hb))]
+        pa.pa_swap_blocks(host_k, host_v, kc, vc,
+                          torch.tensor(list(zip(hb, table)), dtype=torch.int64, device=dev))
+        after = probe(table, len(h), qp)
+        torch.cuda.synchronize()
+        assert torch.equal(before, after), f"sequence {v} decodes differently after its swap"
+        host_free.extend(hb)
+        hist[v] = h
+        order.append(v)
+        del swapped[v]
+        stats["swap_in"] += 1
+        return True
 
     def write(tags, slots):
         o = torch.tensor([t[0] for t in tags])
@@ -46,6 +94,10 @@ def test_continuous_batching_steps():
                                 torch.tensor(slots, dtype=torch.int64, device=dev))
 
     for step in range(40):
+        # swapped-out sequences come back first, oldest first, while the pool has room
+        for v in sorted(swapped):
+            if not swap_in(v):
+                break
         # arrivals
         for _ in range(int(rng.integers(0, 3)) if order else 2):
             if next_id >= MAX_ORIGINS:
@@ -83,6 +135,8 @@ def test_continuous_batching_steps():
                 except pa.NoSpace:
                     waiting = [v for v in order if v != s and v not in stepped]
                     victim = waiting[-1] if waiting else s
+                    if victim == s or not swap_out(victim):
+                        pass                         # no room on the host: the victim is dropped
                     bm.preempt(victim)
                     order.remove(victim)
                     del hist[victim]
@@ -135,3 +189,4 @@ def test_continuous_batching_steps():
         stats["checked"] += 1
     print(stats, flush=True)
     assert stats["cow"] > 0 and stats["preempt"] > 0 and stats["fork"] > 0 and stats["checked"] >= 30
+    assert stats["swap_out"] > 0 and stats["swap_in"] > 0
