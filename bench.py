@@ -81,9 +81,13 @@ def main() -> int:
     ap.add_argument("--prefill-chunk", type=int, default=512,
                     help="--op prefill: query tokens per sequence (its last min(L, chunk) tokens)")
     ap.add_argument("--workload", default="llama8b_gqa_bf16")
-    ap.add_argument("--kernel", choices=("partitioned", "single", "cascade"), default="partitioned",
-                    help="cascade: pa_decode_cascade over the prefix every table shares "
-                         "(shared-prefix workloads only)")
+    ap.add_argument("--kernel", choices=("step", "balanced", "partitioned", "single", "cascade"),
+                    default="step",
+                    help="step: pa_decode_step, the cache write and the work-balanced attention in "
+                         "one call (default); balanced: pa_reshape_and_cache then "
+                         "pa_decode_balanced; partitioned / single: pa_reshape_and_cache then "
+                         "pa_decode_partitioned / pa_decode; cascade: pa_decode_cascade over the "
+                         "prefix every table shares (shared-prefix workloads only)")
     ap.add_argument("--partition-size", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--stream-read-mib", type=int, default=2048,
@@ -172,14 +176,29 @@ def main() -> int:
             slots=torch.from_numpy(w.slot_mapping).to(dev),
             out=torch.empty((S, Hq, D), dtype=torch.float32, device=dev),
             ws=pa.cascade_workspace(S, Hq, D, mcl, psize, npb, device=dev) if npb
+            else pa.balanced_workspace(Hq, Hkv, D, device=dev) if args.kernel in ("step", "balanced")
             else pa.decode_workspace(S, Hq, D, mcl, psize, device=dev)))
+        per = spec.new_tokens_per_seq
+        last = torch.arange(S, device=dev) * per + (per - 1)
+        early = torch.ones(S * per, dtype=torch.bool, device=dev)
+        early[last] = False
+        inputs[-1].update(
+            new_key=w.key[last].contiguous(), new_value=w.value[last].contiguous(),
+            early_key=w.key[early].contiguous(), early_value=w.value[early].contiguous(),
+            early_slots=inputs[-1]["slots"][early].contiguous())
     torch.cuda.synchronize()
     log(f"[bench] {args.workload}: S={S} Hq={Hq} Hkv={Hkv} D={D} sum(L)={int(base.context_lens.sum())} "
         f"KV bytes/step={kv_bytes / 1e6:.1f} MB, replicas={args.replicas}, kernel={args.kernel}, P={psize}")
 
     def attention(x):
         w = x["w"]
-        if args.kernel == "single":
+        if args.kernel == "step":
+            pa.pa_decode_step(x["out"], w.query, x["new_key"], x["new_value"], w.key_cache,
+                              w.value_cache, x["bt"], x["cl"], w.scale, x["ws"])
+        elif args.kernel == "balanced":
+            pa.pa_decode_balanced(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"],
+                                  w.scale, x["ws"])
+        elif args.kernel == "single":
             pa.pa_decode(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"], w.scale)
         elif args.kernel == "cascade":
             pa.pa_decode_cascade(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"],
@@ -191,7 +210,12 @@ def main() -> int:
     def step(i, ev=None):
         x = inputs[i % len(inputs)]
         w = x["w"]
-        pa.pa_reshape_and_cache(w.key, w.value, w.key_cache, w.value_cache, x["slots"])
+        if args.kernel != "step":
+            pa.pa_reshape_and_cache(w.key, w.value, w.key_cache, w.value_cache, x["slots"])
+        elif x["early_slots"].numel():
+            # several new tokens per sequence: all but the last go through the cache write
+            pa.pa_reshape_and_cache(x["early_key"], x["early_value"], w.key_cache, w.value_cache,
+                                    x["early_slots"])
         if ev is not None:
             ev[0].record()
         attention(x)
@@ -258,12 +282,14 @@ def main() -> int:
             "head_size": D, "block_size": 16, "sum_context_len": int(base.context_lens.sum()),
             "max_context_len": mcl, "kv_bytes_per_step": kv_bytes,
             "kernel": {"single": "pa_decode", "partitioned": "pa_decode_partitioned",
-                       "cascade": "pa_decode_cascade"}[args.kernel],
-            "partition_size": psize if args.kernel != "single" else None,
+                       "cascade": "pa_decode_cascade", "balanced": "pa_decode_balanced",
+                       "step": "pa_decode_step"}[args.kernel],
+            "partition_size": psize if args.kernel in ("partitioned", "cascade") else None,
             "unique_kv_bytes_per_step": unique_bytes,
             "prefix_blocks": npb or None,
             "replicas": args.replicas, "pool_blocks": base.num_blocks,
-            "step": "pa_reshape_and_cache + attention",
+            "step": "pa_decode_step (cache write fused into the attention call)"
+                    if args.kernel == "step" else "pa_reshape_and_cache + attention",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
@@ -277,7 +303,11 @@ def main() -> int:
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": {"single": "paged_decode_kernel",
+            "kernel": {"step": "attention call: paged_decode_balanced_kernel (cache write "
+                               "fused) + balanced_reduce_kernel",
+                       "balanced": "attention call: paged_decode_balanced_kernel + "
+                                   "balanced_reduce_kernel",
+                       "single": "paged_decode_kernel",
                        "partitioned": "attention call: paged_decode_persistent_kernel + "
                                       "lse_reduce_kernel",
                        "cascade": "attention call: cascade_prefix_kernel + "

@@ -17,6 +17,10 @@
  *   pa_decode_partitioned  the same result, with each context cut into
  *                          fixed-size partitions that run in parallel and a
  *                          log-sum-exp reduce across partitions
+ *   pa_decode_balanced     the same result with the work cut into equal
+ *                          byte ranges over the whole batch
+ *   pa_decode_step         cache write of each sequence's new token plus
+ *                          balanced decode, in one call
  *   pa_decode_cascade      the same result for a batch whose tables all begin
  *                          with the same physical blocks (a shared prefix):
  *                          the prefix is read once per KV head for the whole
@@ -282,6 +286,81 @@ pa_status_t pa_decode_partitioned_noalloc(void* out, pa_dtype_t out_dtype, const
                                           int head_size, int block_size, int64_t num_blocks,
                                           float scale, int max_context_len, int partition_size,
                                           void* stream);
+
+/*
+ * Workspace bytes pa_decode_balanced and pa_decode_step need: with
+ * G = num_q_heads / num_kv_heads and W = 1024 (the most workgroups a call
+ * launches), 256-byte-aligned arrays of W 16-byte descriptors, then float32
+ * part_max [2W][G], part_sum [2W][G] and part_out [2W][G][head_size]. It does
+ * not depend on the batch. Returns 0 for arguments out of range.
+ */
+size_t pa_decode_balanced_workspace_size(int num_q_heads, int num_kv_heads, int head_size);
+
+/*
+ * pa_decode_balanced -- paged decode attention with the work split evenly by
+ * bytes read, not by sequence.
+ *
+ * Same inputs and result as pa_decode (the attention of each sequence's query
+ * over all L = context_lens[s] tokens of its context, read through its block
+ * table: "The idea vLLM started from: pages" on "What vLLM Is and Why It
+ * Exists"). Contexts of very different lengths share one step (the pages'
+ * traffic is mostly short requests and a few long ones, "The problem a naive
+ * server has"), so the 16-token blocks of every (sequence, KV head) row are
+ * laid end to end and cut into equal contiguous ranges: one per resident
+ * workgroup, and within it one per wave. A row split between ranges is
+ * finished with the log-sum-exp combination of its pieces (as
+ * pa_decode_partitioned combines partitions) in a fixed order, by the
+ * workgroup itself when the split is inside it, else by a second small
+ * kernel. The result equals pa_decode up to fp32 rounding order; it depends
+ * only on the context lengths and the number of compute units, never on
+ * block placement, and repeats bit for bit.
+ *
+ *   workspace  device scratch of at least pa_decode_balanced_workspace_size()
+ *              bytes, 256-byte aligned; its contents before the call do not
+ *              matter and are unspecified after it. Two calls sharing a
+ *              workspace must not overlap in time.
+ *   num_seqs   0 .. 4096 (PA_EUNSUPPORTED above), and
+ *              num_seqs * num_kv_heads * max_blocks_per_seq < 2^31.
+ * Other arguments, checks, errors and the NaN rows of unreadable contexts
+ * (longer than 16 * max_blocks_per_seq tokens, or reaching a block id outside
+ * [0, NB)) are those of pa_decode.
+ */
+pa_status_t pa_decode_balanced(void* out, pa_dtype_t out_dtype, const void* query,
+                               const void* key_cache, const void* value_cache, pa_dtype_t kv_dtype,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                               float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_step -- one decode step in one call: write each sequence's new
+ * token into the cache and attend over the context that includes it.
+ *
+ * Each request keeps the key/value vectors of every token it produced ("The
+ * problem a naive server has", point 3, on "What vLLM Is and Why It Exists").
+ * For every sequence s with L = context_lens[s] >= 1 (L counts the new
+ * token), key[s][h][:] and value[s][h][:] are written into row (L - 1) % 16 of
+ * physical block block_tables[s][(L - 1) / 16] of both pools, for every KV
+ * head h -- exactly what pa_reshape_and_cache does with slot =
+ * block_tables[s][(L - 1) / 16] * 16 + (L - 1) % 16 -- and out is the
+ * attention of pa_decode_balanced over the L tokens, the new one included
+ * (taken from key/value directly, so the result does not depend on when the
+ * write lands). A sequence with L = 0, an unreadable context, or a table entry
+ * for position L - 1 outside [0, NB) writes nothing.
+ *
+ *   key, value  [S][Hkv][D] of kv_dtype (device), 16-byte aligned.
+ *   key_cache, value_cache  updated in place (one slot per sequence).
+ * The block holding position L - 1 must not be shared with another sequence
+ * in the call (copy-on-write first: pa_copy_blocks). Other arguments, checks
+ * and errors as pa_decode_balanced; key or value null with num_seqs > 0 is
+ * PA_EINVAL.
+ */
+pa_status_t pa_decode_step(void* out, pa_dtype_t out_dtype, const void* query, const void* key,
+                           const void* value, void* key_cache, void* value_cache,
+                           pa_dtype_t kv_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes pa_decode_cascade needs. With

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_cache.hip", "pa_cascade.hip", "pa_prefill.hip",
-           "pa_stream.hip", "pa_block_manager.cpp", "pa_device_cache.cpp", "pa_noalloc.hip"]
+           "pa_stream.hip", "pa_block_manager.cpp", "pa_device_cache.cpp", "pa_noalloc.hip",
+           "pa_decode_balanced.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

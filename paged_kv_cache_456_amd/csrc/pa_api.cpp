@@ -366,6 +366,111 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
     return from_hip(pa::launch_reduce(r, head_size, out_dtype == PA_BF16, num_seqs, s));
 }
 
+// Workspace of the balanced decode: descriptors, then the partials of the at
+// most two cut rows of each workgroup.
+struct BalancedWorkspace {
+    size_t desc, part_max, part_sum, part_out, total;
+};
+
+static BalancedWorkspace balanced_layout(int group, int head_size) {
+    const size_t slots = 2 * static_cast<size_t>(pa::kMaxBalancedWorkgroups) * group;
+    BalancedWorkspace w{};
+    w.desc = 0;
+    w.part_max = align256(sizeof(int4) * pa::kMaxBalancedWorkgroups);
+    w.part_sum = w.part_max + align256(sizeof(float) * slots);
+    w.part_out = w.part_sum + align256(sizeof(float) * slots);
+    w.total = w.part_out + align256(sizeof(float) * slots * head_size);
+    return w;
+}
+
+size_t pa_decode_balanced_workspace_size(int num_q_heads, int num_kv_heads, int head_size) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || num_q_heads % num_kv_heads != 0 ||
+        num_q_heads / num_kv_heads > kMaxGroup || head_size > 4096)
+        return 0;
+    return balanced_layout(num_q_heads / num_kv_heads, head_size).total;
+}
+
+// Shared by pa_decode_balanced and pa_decode_step (new_key = nullptr: no write).
+static pa_status_t decode_balanced(void* out, pa_dtype_t out_dtype, const void* query,
+                                   const void* new_key, const void* new_value, void* key_cache,
+                                   void* value_cache, pa_dtype_t kv_dtype,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_size, int block_size,
+                                   int64_t num_blocks, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    pa_status_t st = check_decode(out, out_dtype, query, key_cache, value_cache, kv_dtype,
+                                  block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
+                                  scale);
+    if (st != PA_OK)
+        return st;
+    if (num_seqs > pa::kMaxBalancedSeqs ||
+        static_cast<int64_t>(num_seqs) * num_kv_heads * max_blocks_per_seq > INT32_MAX)
+        return PA_EUNSUPPORTED;
+    if (num_seqs == 0)
+        return PA_OK;
+    if (new_key != nullptr || new_value != nullptr) {
+        if (!new_key || !new_value || !aligned(new_key, 16) || !aligned(new_value, 16))
+            return PA_EINVAL;
+    }
+    const size_t need = pa_decode_balanced_workspace_size(num_q_heads, num_kv_heads, head_size);
+    if (!workspace || workspace_bytes < need)
+        return PA_EWORKSPACE;
+    if (!aligned(workspace, 256))
+        return PA_EINVAL;
+    const BalancedWorkspace lay = balanced_layout(num_q_heads / num_kv_heads, head_size);
+    char* ws = static_cast<char*>(workspace);
+    pa::BalancedParams bp{};
+    bp.d = make_params(query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_q_heads, num_kv_heads, num_blocks, scale);
+    bp.d.out = out;
+    bp.d.part_max = reinterpret_cast<float*>(ws + lay.part_max);
+    bp.d.part_sum = reinterpret_cast<float*>(ws + lay.part_sum);
+    bp.d.part_out = reinterpret_cast<float*>(ws + lay.part_out);
+    bp.d.num_seqs = num_seqs;
+    bp.d.num_partitions = 1;
+    bp.d.partition_blocks = max_blocks_per_seq;
+    bp.d.table_blocks = max_blocks_per_seq;
+    bp.desc = reinterpret_cast<int4*>(ws + lay.desc);
+    bp.new_key = new_key;
+    bp.new_value = new_value;
+    // At least two units per wave when every context fills its table.
+    const int64_t bound = static_cast<int64_t>(num_seqs) * num_kv_heads * max_blocks_per_seq;
+    const int64_t per_wg = 2 * static_cast<int64_t>(pa::kBalancedWaves);
+    const int max_wgs = static_cast<int>((bound + per_wg - 1) / per_wg);
+    return from_hip(pa::launch_decode_balanced(bp, kv_dtype == PA_BF16, head_size,
+                                               out_dtype == PA_BF16, max_wgs,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_decode_balanced(void* out, pa_dtype_t out_dtype, const void* query,
+                               const void* key_cache, const void* value_cache, pa_dtype_t kv_dtype,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                               float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_balanced(out, out_dtype, query, nullptr, nullptr, const_cast<void*>(key_cache),
+                           const_cast<void*>(value_cache), kv_dtype, block_tables,
+                           max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                           head_size, block_size, num_blocks, scale, workspace, workspace_bytes,
+                           stream);
+}
+
+pa_status_t pa_decode_step(void* out, pa_dtype_t out_dtype, const void* query, const void* key,
+                           const void* value, void* key_cache, void* value_cache,
+                           pa_dtype_t kv_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && (!key || !value))
+        return PA_EINVAL;
+    return decode_balanced(out, out_dtype, query, key, value, key_cache, value_cache, kv_dtype,
+                           block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                           num_kv_heads, head_size, block_size, num_blocks, scale, workspace,
+                           workspace_bytes, stream);
+}
+
 // Partitions of a cascade call: the suffix partitions (tokens past the shared
 // prefix, at most max_context_len - 16 * num_prefix_blocks) and one slot per
 // prefix chunk.

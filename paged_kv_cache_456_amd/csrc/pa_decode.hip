@@ -18,25 +18,8 @@
 // item. An item's blocks are dealt out in rounds: in each round, wave w takes
 // BPW consecutive blocks.
 //
-// Per round, per wave:
-//   * physical block ids come from a per-wave register holding the wave's
-//     slice of the block table (one vector load per 64 entries, v_readlane
-//     per block), so each table entry is resolved once per wavefront;
-//   * the K and V tiles of all BPW blocks (16 tokens x D of one KV head, a
-//     contiguous run in the pool) are requested together, before any of them
-//     is used, and the next round's tiles are requested while this round is
-//     computed (K as soon as Q^T K has consumed the K registers, V after P.V);
-//   * K is loaded so that lane l holds token l%16, 16-byte chunks l/16+4c of
-//     its row: the B-operand layout of a 16x16 MFMA. Q^T K for the whole head
-//     group is an MFMA chain (bf16: v_mfma_f32_16x16x32_bf16, fp32:
-//     v_mfma_f32_16x16x4_f32), heads as rows, tokens as columns;
-//   * softmax statistics are kept online (running max and sum, base-2
-//     exponent with scale*log2(e) folded in); the round max is an in-lane max
-//     over the BPW blocks followed by a 16-lane DPP row reduction;
-//   * V is loaded fully coalesced (consecutive lanes read consecutive 16-byte
-//     chunks); P.V runs on the VALU in fp32 with P in fp32 (P rounded to bf16
-//     would cost about 2e-3 of accuracy). P moves from the MFMA layout to the
-//     V layout through a small per-wave LDS tile.
+// The per-round work of a wave (table resolve, K/V streaming, Q^T K on MFMA,
+// online softmax, P.V) is in pa_decode_core.h.
 // The waves then merge their (max, sum, output) through LDS in a fixed order.
 //
 // Split contexts. A sequence with a single partition writes its output row
@@ -47,151 +30,12 @@
 // positions, so results never depend on where the blocks sit in the pool.
 #include <algorithm>
 
-#include "pa_internal.h"
+#include "pa_decode_core.h"
 
 namespace pa {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// DPP controls (GFX9 encoding).
-constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Max / sum over the 16 lanes of a DPP row; every lane of the row gets the
-// result (the combining order is the same in every lane).
-__device__ __forceinline__ float row_max16(float x) {
-    x = fmaxf(x, dpp<kQuadSwap1>(x));
-    x = fmaxf(x, dpp<kQuadSwap2>(x));
-    x = fmaxf(x, dpp<kRowHalfMirror>(x));
-    x = fmaxf(x, dpp<kRowMirror>(x));
-    return x;
-}
-
-__device__ __forceinline__ float row_sum16(float x) {
-    x = x + dpp<kQuadSwap1>(x);
-    x = x + dpp<kQuadSwap2>(x);
-    x = x + dpp<kRowHalfMirror>(x);
-    x = x + dpp<kRowMirror>(x);
-    return x;
-}
-
-__device__ __forceinline__ float readlane_f(float x, int lane) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
-}
-
-__device__ __forceinline__ u32x4 ld16(const char* p) {
-    return *reinterpret_cast<const u32x4*>(p);
-}
-
-// KV tiles are read once per step: stream them past the caches.
-__device__ __forceinline__ u32x4 ld16_stream(const char* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
-// Make this wave's LDS writes visible to its own later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// fp32 -> bf16, round to nearest even, NaN kept NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-}
-
-template <typename OUT>
-__device__ __forceinline__ void store_out(void* base, int64_t idx, float v);
-template <>
-__device__ __forceinline__ void store_out<F32>(void* base, int64_t idx, float v) {
-    static_cast<float*>(base)[idx] = v;
-}
-template <>
-__device__ __forceinline__ void store_out<BF16>(void* base, int64_t idx, float v) {
-    static_cast<uint16_t*>(base)[idx] = f32_to_bf16(v);
-}
-
-template <typename KV>
-struct Ops;
-
-template <>
-struct Ops<BF16> {
-    __device__ static __forceinline__ void to_f32(const u32x4& c, float (&f)[8]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(c[i] << 16);
-            f[2 * i + 1] = __uint_as_float(c[i] & 0xFFFF0000u);
-        }
-    }
-    // acc[head][token] += q[head][k-chunk] . K[token][k-chunk] for 8 elements.
-    __device__ static __forceinline__ f32x4 qk(const u32x4& q, const u32x4& k, f32x4 acc) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, q),
-                                                       __builtin_bit_cast(bf16x8, k), acc, 0, 0, 0);
-    }
-};
-
-template <>
-struct Ops<F32> {
-    __device__ static __forceinline__ void to_f32(const u32x4& c, float (&f)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            f[i] = __uint_as_float(c[i]);
-    }
-    __device__ static __forceinline__ f32x4 qk(const u32x4& q, const u32x4& k, f32x4 acc) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(q[e]), __uint_as_float(k[e]),
-                                                       acc, 0, 0, 0);
-        return acc;
-    }
-};
-
-template <typename KV, int D>
-struct Geometry {
-    static constexpr int kRow = D * KV::kBytes;          // bytes per token row
-    static constexpr int kTile = kBlockSize * kRow;      // bytes per (block, head) tile
-    static constexpr int kCh = kRow / 16;                // 16-byte chunks per row
-    static constexpr int kNq = kCh / 4;                  // K chunks per lane per tile
-    static constexpr int kTpl = kWave / kCh;             // token rows per coalesced V load
-    static constexpr int kNv = kBlockSize / kTpl;        // V chunks per lane per tile
-    static constexpr int kEpc = 16 / KV::kBytes;         // elements per chunk
-    static_assert(kNq == kNv, "K and V take the same number of loads");
-    static_assert(kCh >= 4 && kCh <= kWave, "row must span 4..64 chunks");
-};
-
-// A context that cannot be read -- longer than its block table or than the
-// partitions of the launch, or a non-empty context in an empty pool -- gets
-// an all-NaN output row. Both kernels apply the same rule.
-__device__ __forceinline__ bool context_unreadable(int L, int max_blocks_per_seq, int num_partitions,
-                                                   int partition_blocks, int64_t num_blocks) {
-    const int64_t cap = min(static_cast<int64_t>(max_blocks_per_seq),
-                            static_cast<int64_t>(num_partitions) * partition_blocks) * kBlockSize;
-    return L < 0 || static_cast<int64_t>(L) > cap || (L > 0 && num_blocks <= 0);
-}
-
-// Tokens of a context that this call reads: those past the skipped leading
-// blocks; -1 (unreadable) when the context is shorter than what is skipped.
-__device__ __forceinline__ int call_len(int L, int skip_blocks) {
-    const int64_t skip = static_cast<int64_t>(skip_blocks) * kBlockSize;
-    return L < skip ? -1 : static_cast<int>(L - skip);
-}
+using namespace core;
 
 // Writes the output rows of the head group of KV head `kvh` of sequence `s`
 // when its context has nothing to read: zeros for an empty context, NaN for
@@ -214,249 +58,33 @@ template <typename KV, int D, int GMAX, typename OUT>
 __device__ __forceinline__ void process_range(const DecodeParams& p, float* smem, int kvh, int s,
                                               int L, int pb0, int pb1, int slot, bool direct) {
     using Gm = Geometry<KV, D>;
-    using Op = Ops<KV>;
-    constexpr int NQ = Gm::kNq, NV = Gm::kNv, CH = Gm::kCh, TPL = Gm::kTpl, EPC = Gm::kEpc;
-    constexpr int ROW = Gm::kRow, TILE = Gm::kTile;
+    constexpr int CH = Gm::kCh, EPC = Gm::kEpc;
     constexpr int BPW = decode_bpw(KV::kBytes, D, GMAX);
     constexpr int GP = decode_pstride(GMAX);
-    constexpr int RPB = kWave / BPW;              // rounds covered by one batch of table entries
 
-    const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nw = blockDim.x / kWave;
-    const int Hq = p.num_q_heads, Hkv = p.num_kv_heads, G = p.group;
-
-    const int tok_end = min(pb1 * kBlockSize, L);
     const int per_round = nw * BPW;
     const int rounds = (pb1 - pb0 + per_round - 1) / per_round;
-    const int wb0 = pb0 + wave * BPW;            // this wave's first block of round 0
+    u32x4 qa[Gm::kNq];
+    load_query<KV, D>(p, kvh, s, qa);
+    WaveAcc<KV, D, GMAX> acc;
+    acc.reset();
+    accumulate_blocks<KV, D, GMAX>(p, smem + wave * (BPW * kBlockSize * GP), qa, kvh, s, L, pb1,
+                                   pb0 + wave * BPW, per_round, rounds, acc);
 
+    const int lane = threadIdx.x & (kWave - 1);
+    const int Hq = p.num_q_heads, G = p.group;
     const int g = lane >> 4;       // MFMA lane group: output rows 4g..4g+3
-    const int r16 = lane & 15;     // MFMA row/column index: A-operand head, token column
+    const int r16 = lane & 15;
     const int vchunk = lane % CH;  // V layout: chunk within the row
     const int vrow = lane / CH;    //           first token row
 
-    // Query rows of the head group as the MFMA A operand (rows >= G are zero).
-    u32x4 qa[NQ];
-    {
-        const bool live = r16 < G;
-        const char* qp = static_cast<const char*>(p.q) +
-                         ((int64_t)s * Hq + (int64_t)kvh * G + (live ? r16 : 0)) * ROW;
-#pragma unroll
-        for (int c = 0; c < NQ; ++c)
-            qa[c] = live ? ld16(qp + (g + 4 * c) * 16) : u32x4{0u, 0u, 0u, 0u};
-    }
-
-    const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE;
-    const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE;
-    const int64_t blk_stride = (int64_t)Hkv * TILE;
-    const int koff = r16 * ROW + g * 16;            // + 64 c
-    const int voff = vrow * ROW + vchunk * 16;      // + TPL * ROW * c
-    const int64_t tbl = (int64_t)s * p.max_blocks_per_seq + p.skip_blocks;
-
-    float m[4], lsum[4];
-    float o[GMAX][EPC];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        m[j] = -INFINITY;
-        lsum[j] = 0.0f;
-    }
-#pragma unroll
-    for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e)
-            o[h][e] = 0.0f;
-
-    float* p_lds = smem + wave * (BPW * kBlockSize * GP);
-    bool poisoned = false;
-
-    // Table entries of rounds [r0, r0 + RPB): lane i holds block b = i % BPW of
-    // round r0 + i / BPW. An entry inside the context that lies outside the
-    // pool marks the wave poisoned (its output becomes NaN) and is replaced by
-    // block 0, so that every load stays inside the pool.
-    int phys_l = 0;
-    int batch_r0 = 0;
-    auto load_entries = [&](int r0) {
-        const int jb = wb0 + (r0 + lane / BPW) * per_round + lane % BPW;
-        const bool mine = jb < pb1;
-        const int e = mine ? p.block_tables[tbl + jb] : 0;
-        const bool bad = e < 0 || static_cast<int64_t>(e) >= p.num_blocks;
-        phys_l = bad ? 0 : e;
-        batch_r0 = r0;
-        if (__ballot(bad) != 0)
-            poisoned = true;
-    };
-    auto block_of = [&](int r, int b) { return wb0 + r * per_round + b; };   // logical block
-    // Slots of a round past the partition's end re-read the partition's last
-    // tile (one that is read anyway, so the extra reads hit in cache) and are
-    // masked out afterwards. Every slot is loaded, so no load sits under a
-    // branch and the compiler can wait for each tile precisely.
-    int last_phys = p.block_tables[tbl + pb1 - 1];
-    if (last_phys < 0 || static_cast<int64_t>(last_phys) >= p.num_blocks) {
-        poisoned = true;
-        last_phys = 0;
-    }
-    auto phys_of = [&](int r, int b) {
-        const int v = __builtin_amdgcn_readlane(phys_l, (r - batch_r0) * BPW + b);
-        return block_of(r, b) < pb1 ? v : last_phys;
-    };
-
-    u32x4 kt[BPW][NQ], vt[BPW][NV];
-    auto issue_k = [&](int r) {
-#pragma unroll
-        for (int b = 0; b < BPW; ++b) {
-            const char* kb = kbase + (int64_t)phys_of(r, b) * blk_stride + koff;
-#pragma unroll
-            for (int c = 0; c < NQ; ++c)
-                kt[b][c] = ld16_stream(kb + 64 * c);
-        }
-    };
-    auto issue_v = [&](int r) {
-#pragma unroll
-        for (int b = 0; b < BPW; ++b) {
-            const char* vb = vbase + (int64_t)phys_of(r, b) * blk_stride + voff;
-#pragma unroll
-            for (int c = 0; c < NV; ++c)
-                vt[b][c] = ld16_stream(vb + TPL * ROW * c);
-        }
-    };
-
-    // One round: Q^T K, online softmax and P.V over this wave's BPW slots. The
-    // following round's K is requested as soon as the K registers are consumed
-    // and its V once P.V is done.
-    auto round = [&](int r) {
-        const int nvb = min(BPW, max(0, pb1 - block_of(r, 0)));   // this wave's blocks this round
-        // ---- logits of the round's slots: heads 4g+j, token column r16
-        f32x4 acc[BPW];
-#pragma unroll
-        for (int b = 0; b < BPW; ++b) {
-            acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int c = 0; c < NQ; ++c)
-                acc[b] = Op::qk(qa[c], kt[b][c], acc[b]);
-        }
-        if (r + 1 < rounds) {
-            if (r + 1 - batch_r0 >= RPB)
-                load_entries(r + 1);
-            issue_k(r + 1);
-        }
-        if (nvb > 0) {
-            // ---- online softmax over the round
-            float x[BPW][4];
-            float alpha[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int b = 0; b < BPW; ++b) {
-                    const bool tvalid = block_of(r, b) * kBlockSize + r16 < tok_end;
-                    x[b][j] = tvalid ? acc[b][j] * p.scale_log2 : -INFINITY;
-                    mx = fmaxf(mx, x[b][j]);
-                }
-                const float mn = fmaxf(m[j], row_max16(mx));
-                alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
-                float ps = 0.0f;
-#pragma unroll
-                for (int b = 0; b < BPW; ++b) {
-                    x[b][j] = __builtin_amdgcn_exp2f(x[b][j] - mn);
-                    ps += x[b][j];
-                }
-                lsum[j] = lsum[j] * alpha[j] + ps;
-                m[j] = mn;
-            }
-            if (4 * g < GP) {
-#pragma unroll
-                for (int b = 0; b < BPW; ++b)
-                    *reinterpret_cast<f32x4*>(p_lds + (b * kBlockSize + r16) * GP + 4 * g) =
-                        f32x4{x[b][0], x[b][1], x[b][2], x[b][3]};
-            }
-            float al[GMAX];
-#pragma unroll
-            for (int h = 0; h < GMAX; ++h)
-                al[h] = readlane_f(alpha[h & 3], 16 * (h >> 2));
-            wave_lds_sync();
-#pragma unroll
-            for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-                for (int e = 0; e < EPC; ++e)
-                    o[h][e] *= al[h];
-            // ---- P.V
-#pragma unroll
-            for (int b = 0; b < BPW; ++b) {
-                // Valid rows of the slot: 16 for a full block, fewer for the
-                // context's last block, none (<= 0) for a slot past the end.
-                const int tvalid = tok_end - block_of(r, b) * kBlockSize;
-#pragma unroll
-                for (int c = 0; c < NV; ++c) {
-                    const int tr = vrow + TPL * c;
-                    const float* prow = p_lds + (b * kBlockSize + tr) * GP;
-                    float pv[GMAX];
-                    if constexpr (GMAX >= 4) {
-#pragma unroll
-                        for (int h4 = 0; h4 < GMAX; h4 += 4) {
-                            const f32x4 q4 = *reinterpret_cast<const f32x4*>(prow + h4);
-                            pv[h4] = q4[0];
-                            pv[h4 + 1] = q4[1];
-                            pv[h4 + 2] = q4[2];
-                            pv[h4 + 3] = q4[3];
-                        }
-                    } else {
-#pragma unroll
-                        for (int h = 0; h < GMAX; ++h)
-                            pv[h] = prow[h];
-                    }
-                    float vf[EPC];
-                    Op::to_f32(vt[b][c], vf);
-                    if (tvalid < kBlockSize && tr >= tvalid) {
-                        // Tail rows may hold anything (even NaN): drop them, do not scale by 0.
-#pragma unroll
-                        for (int e = 0; e < EPC; ++e)
-                            vf[e] = 0.0f;
-                    }
-#pragma unroll
-                    for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-                        for (int e = 0; e < EPC; ++e)
-                            o[h][e] = fmaf(pv[h], vf[e], o[h][e]);
-                }
-            }
-            wave_lds_sync();
-        }
-        if (r + 1 < rounds)
-            issue_v(r + 1);
-    };
-
-    load_entries(0);
-    issue_k(0);
-    issue_v(0);
-#pragma nounroll
-    for (int r = 0; r < rounds; ++r)
-        round(r);
-
     // Wave totals: sums over the 16 token columns, outputs over the token rows.
     float srow[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        srow[j] = row_sum16(lsum[j]);
-#pragma unroll
-    for (int off = CH; off < kWave; off <<= 1)
-#pragma unroll
-        for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e)
-                o[h][e] += __shfl_xor(o[h][e], off, kWave);
-    if (poisoned) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            m[j] = 0.0f;
-            srow[j] = __builtin_nanf("");
-        }
-#pragma unroll
-        for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e)
-                o[h][e] = __builtin_nanf("");
-    }
+    wave_totals<KV, D, GMAX>(acc, srow);
+    float (&m)[4] = acc.m;
+    float (&o)[GMAX][EPC] = acc.o;
 
     float* red_m = smem + nw * (BPW * kBlockSize * GP);
     float* red_s = red_m + nw * GP;
@@ -490,18 +118,18 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, float* smem
         float M = -INFINITY;
         for (int w = 0; w < nw; ++w)
             M = fmaxf(M, red_m[w * GP + h]);
-        float S = 0.0f, acc = 0.0f;
+        float S = 0.0f, od = 0.0f;
         for (int w = 0; w < nw; ++w) {
             const float f = __builtin_amdgcn_exp2f(red_m[w * GP + h] - M);
             S = fmaf(red_s[w * GP + h], f, S);
-            acc = fmaf(red_o[(w * GMAX + h) * D + d], f, acc);
+            od = fmaf(red_o[(w * GMAX + h) * D + d], f, od);
         }
         const int64_t row = (int64_t)s * Hq + (int64_t)kvh * G + h;
         if (!split) {
-            store_out<OUT>(p.out, row * D + d, acc / S);
+            store_out<OUT>(p.out, row * D + d, od / S);
         } else {
             const int64_t pi = row * p.part_stride + slot;
-            p.part_out[pi * D + d] = acc / S;
+            p.part_out[pi * D + d] = od / S;
             if (d == 0) {
                 p.part_max[pi] = M * kLn2;
                 p.part_sum[pi] = S;

@@ -90,13 +90,12 @@ constexpr int decode_gmax(int group) {
     return group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : group <= 8 ? 8 : 16;
 }
 
-// Blocks each wave loads per round. A round's K and V tiles sit in registers
-// together (8 * D * elem_bytes / 64 bytes of VGPRs per lane per block); two
-// blocks of bf16 D = 128 keep 16 KB in flight per wave. Wide rows and large
-// head groups take one.
-constexpr int decode_bpw(int elem_bytes, int head_size, int gmax) {
-    return (gmax > 8 || head_size * elem_bytes > 256) ? 1 : 2;
-}
+// Blocks each wave loads per round. One: the next round's K and V tiles are
+// requested while a round computes, so a wave keeps one to two blocks (8-16
+// KB for bf16 D = 128) in flight; measured on MI355X, more requests in flight
+// per wave (two blocks per round) saturate the L1 address translation's
+// in-flight tracking and run slower.
+constexpr int decode_bpw(int /*elem_bytes*/, int /*head_size*/, int /*gmax*/) { return 1; }
 
 // Row stride, in floats, of the per-wave softmax-weight tile in LDS.
 constexpr int decode_pstride(int gmax) { return gmax < 4 ? 4 : gmax; }
@@ -127,6 +126,22 @@ constexpr int kMaxPersistentKvHeads = 256;
 constexpr size_t persistent_lds_bytes(int num_seqs) {
     return sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1 + 2 * kItemListCap);
 }
+
+// Work-balanced decode (pa_decode_balanced.hip): the (sequence, KV head,
+// block) units of the batch cut into equal contiguous ranges, one per
+// resident workgroup and, within it, one per wave.
+constexpr int kBalancedWaves = 4;               // waves per workgroup
+constexpr int kMaxBalancedWorkgroups = 1024;    // grid cap; sizes the workspace
+constexpr int kMaxBalancedSeqs = 4096;          // first units of all sequences sit in LDS
+
+struct BalancedParams {
+    DecodeParams d;                // part_max / part_sum: [2 * wgs][group] (max in base 2),
+                                   // part_out: [2 * wgs][group][D]
+    int4* desc;                    // [wgs]: row cut at the end of a workgroup's range, its slot
+                                   // there, and the last workgroup holding it; x < 0 for none
+    const void* new_key;           // [S][Hkv][D]: the step's new token, written at L - 1, or nullptr
+    const void* new_value;
+};
 
 // Shared-prefix (cascade) attention over the blocks every sequence shares.
 struct CascadeParams {
@@ -203,6 +218,11 @@ hipError_t launch_decode(const DecodeParams& p, int kv_bf16, int head_size, int 
                          int num_seqs, int grid_partitions, int waves, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, int head_size, int out_bf16, int num_seqs,
                          hipStream_t stream);
+// The balanced decode and its combining kernel; max_workgroups caps the grid
+// below the resident count (small batches).
+hipError_t launch_decode_balanced(const BalancedParams& p, int kv_bf16, int head_size, int out_bf16,
+                                  int max_workgroups, hipStream_t stream);
+size_t balanced_lds_bytes_for(int kv_bf16, int head_size, int group, int num_seqs);
 hipError_t launch_cache(const CacheParams& p, int64_t num_tokens, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, int64_t num_pairs, hipStream_t stream);
 hipError_t launch_swap_blocks(const SwapParams& p, int64_t num_pairs, hipStream_t stream);

@@ -156,3 +156,42 @@ def check_scatter(w: Workload, g: GpuResult, r: OracleResult, full_pool: bool = 
             changed = set(torch.nonzero(diff).flatten().cpu().tolist())
             written = {int(x) for x in w.slot_mapping if 0 <= x < w.num_blocks * B}
             assert changed <= written, f"slots changed outside the mapping: {sorted(changed - written)[:5]}"
+
+
+def gpu_balanced(w: Workload, step: bool = False, out_dtype=torch.float32, in_place: bool = False,
+                 block_tables: Optional[torch.Tensor] = None,
+                 context_lens: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> GpuResult:
+    """The step on the GPU through the balanced entry points: the cache write with
+    pa_reshape_and_cache then pa_decode_balanced, or (step=True) pa_decode_step writing each
+    sequence's last new token itself (earlier new tokens of a sequence, when it has several,
+    go through pa_reshape_and_cache first)."""
+    bt, cl, slots = device_inputs(w)
+    if block_tables is not None:
+        bt = block_tables
+    if context_lens is not None:
+        cl = context_lens
+    kc = w.key_cache if in_place else w.key_cache.clone()
+    vc = w.value_cache if in_place else w.value_cache.clone()
+    S, Hq, D = w.query.shape
+    Hkv = kc.shape[1]
+    out = torch.empty((S, Hq, D), dtype=out_dtype, device=kc.device)
+    ws = workspace
+    if ws is None:
+        ws = pa.balanced_workspace(Hq, Hkv, D, device=kc.device)
+        ws.fill_(0xFF)                  # NaN bit patterns: the call must not depend on them
+    if not step:
+        pa.pa_reshape_and_cache(w.key, w.value, kc, vc, slots)
+        pa.pa_decode_balanced(out, w.query, kc, vc, bt, cl, w.scale, ws)
+    else:
+        per = w.spec.new_tokens_per_seq
+        idx = torch.arange(S, device=kc.device) * per + (per - 1)
+        if per > 1:
+            keep = torch.ones(S * per, dtype=torch.bool, device=kc.device)
+            keep[idx] = False
+            pa.pa_reshape_and_cache(w.key[keep].contiguous(), w.value[keep].contiguous(), kc, vc,
+                                    slots[keep].contiguous())
+        pa.pa_decode_step(out, w.query, w.key[idx].contiguous(), w.value[idx].contiguous(), kc, vc,
+                          bt, cl, w.scale, ws)
+    torch.cuda.synchronize()
+    return GpuResult(out, kc, vc, ws)

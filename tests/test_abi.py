@@ -162,6 +162,17 @@ def test_noalloc_checks(lib, kw, expect):
     assert noalloc_call(lib, **kw) == expect
 
 
+def test_balanced_workspace_size(lib):
+    a256 = lambda n: (n + 255) // 256 * 256
+    W = 1024
+    for hq, hkv, d in ((32, 8, 128), (64, 8, 128), (4, 4, 64), (16, 1, 64)):
+        G = hq // hkv
+        assert pa.pa_decode_balanced_workspace_size(hq, hkv, d) == \
+            a256(16 * W) + 2 * a256(4 * 2 * W * G) + a256(4 * 2 * W * G * d)
+    assert pa.pa_decode_balanced_workspace_size(6, 4, 64) == 0
+    assert pa.pa_decode_balanced_workspace_size(34, 2, 64) == 0
+
+
 def test_workspace_size_formula(lib):
     a256 = lambda n: (n + 255) // 256 * 256
     for S, Hq, D, L, Ps in [(64, 32, 128, 4096, 256), (8, 64, 128, 32768, 512), (4, 4, 64, 37, 32),
