@@ -63,6 +63,17 @@ __device__ __forceinline__ u32x4 ld16_stream(const char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// A buffer resource over one tile (wave-uniform base, `bytes` long): loads
+// through it take a 32-bit lane offset, and an offset past the end reads 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, 0x00020000);
+}
+
+// 16 bytes at lane offset `off` of a tile, streamed (nontemporal).
+__device__ __forceinline__ u32x4 ld16_tile(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
 // Make this wave's LDS writes visible to its own later LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -215,24 +226,26 @@ __device__ __forceinline__ void accumulate_blocks(const DecodeParams& p, float* 
     const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * TILE;
     const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * TILE;
     const int64_t blk_stride = (int64_t)p.num_kv_heads * TILE;
-    const int koff = r16 * ROW + g * 16;            // + 64 c
-    const int voff = vrow * ROW + vchunk * 16;      // + TPL * ROW * c
+    // Lane offsets inside a tile (loads go through a per-tile buffer resource).
+    const uint32_t koff = static_cast<uint32_t>(r16 * ROW + g * 16);          // + 64 c
+    const uint32_t voff = static_cast<uint32_t>(vrow * ROW + vchunk * 16);    // + TPL * ROW * c
     const int64_t tbl = (int64_t)s * p.max_blocks_per_seq + p.skip_blocks;
 
-    // Table entries, one round ahead of their use: lane i holds the entry of
-    // slot i % BPW of a round. Slots past the run's end re-read its last entry
-    // (and so its last tile, which is read anyway: the extra reads hit in
-    // cache) and are masked out afterwards. An entry outside the pool marks
-    // the wave poisoned (its output becomes NaN) and is replaced by block 0,
-    // so that every load stays inside the pool. Every load of the steady-state
-    // loop below is unconditional, so the compiler can count the loads in
-    // flight and wait for each tile alone: round r + 1's K and V tiles stream
-    // in while round r computes.
+    // Table entries live in a register: lane i holds the entry of slot
+    // i % BPW of round r0 + i / BPW, for the RPL rounds from r0 (one vector
+    // load, refilled every RPL rounds), and v_readlane picks a round's
+    // entries. Slots past the run's end re-read its last entry (and so its
+    // last tile, which is read anyway: the extra reads hit in cache) and are
+    // masked out afterwards. An entry outside the pool marks the wave
+    // poisoned (its output becomes NaN) and is replaced by block 0, so that
+    // every load stays inside the pool. Every load of the steady-state loop
+    // below is unconditional (but for the refill), so the compiler can count
+    // the loads in flight and wait for each tile alone: round r + 1's K and V
+    // tiles stream in while round r computes.
+    constexpr int RPL = kWave / BPW;                  // rounds per entry load
     auto block_of = [&](int r, int b) { return wb0 + r * per_round + b; };   // logical block
-    auto load_entry = [&](int r) {
-        return p.block_tables[tbl + min(block_of(r, lane % BPW), pb1 - 1)];
-    };
-    auto sanitize = [&](int e) {
+    auto load_entries = [&](int r0) {
+        const int e = p.block_tables[tbl + min(block_of(r0 + lane / BPW, lane % BPW), pb1 - 1)];
         const bool bad = e < 0 || static_cast<int64_t>(e) >= p.num_blocks;
         if (__ballot(bad) != 0)
             acc.poisoned = true;
@@ -240,22 +253,25 @@ __device__ __forceinline__ void accumulate_blocks(const DecodeParams& p, float* 
     };
 
     u32x4 kt[BPW][NQ], vt[BPW][NV];
-    auto issue_k = [&](int phys) {
+    int ent = 0;
+    auto issue_k = [&](int r) {
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
-            const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(phys, b) * blk_stride + koff;
+            const int phys = __builtin_amdgcn_readlane(ent, (r % RPL) * BPW + b);
+            const auto rk = tile_rsrc(kbase + (int64_t)phys * blk_stride, TILE);
 #pragma unroll
             for (int c = 0; c < NQ; ++c)
-                kt[b][c] = ld16_stream(kb + 64 * c);
+                kt[b][c] = ld16_tile(rk, koff + 64u * c);
         }
     };
-    auto issue_v = [&](int phys) {
+    auto issue_v = [&](int r) {
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
-            const char* vb = vbase + (int64_t)__builtin_amdgcn_readlane(phys, b) * blk_stride + voff;
+            const int phys = __builtin_amdgcn_readlane(ent, (r % RPL) * BPW + b);
+            const auto rv = tile_rsrc(vbase + (int64_t)phys * blk_stride, TILE);
 #pragma unroll
             for (int c = 0; c < NV; ++c)
-                vt[b][c] = ld16_stream(vb + TPL * ROW * c);
+                vt[b][c] = ld16_tile(rv, voff + static_cast<uint32_t>(TPL * ROW) * c);
         }
     };
 
@@ -263,7 +279,6 @@ __device__ __forceinline__ void accumulate_blocks(const DecodeParams& p, float* 
     // steady state (NEXT) the following round's K is requested as soon as the
     // K registers are consumed, the entries of the round after it right then,
     // and its V once P.V is done.
-    int e_next = 0, phys = 0;
     auto round = [&](int r, auto next_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
         const int nvb = min(BPW, max(0, pb1 - block_of(r, 0)));   // this wave's blocks this round
@@ -276,9 +291,9 @@ __device__ __forceinline__ void accumulate_blocks(const DecodeParams& p, float* 
                 lg[b] = Op::qk(qa[c], kt[b][c], lg[b]);
         }
         if constexpr (NEXT) {
-            phys = sanitize(e_next);
-            issue_k(phys);
-            e_next = load_entry(r + 2);
+            if ((r + 1) % RPL == 0)
+                ent = load_entries(r + 1);
+            issue_k(r + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (nvb > 0) {
@@ -365,19 +380,18 @@ __device__ __forceinline__ void accumulate_blocks(const DecodeParams& p, float* 
         }
         if constexpr (NEXT) {
             __builtin_amdgcn_sched_barrier(0);
-            issue_v(phys);
+            issue_v(r + 1);
         }
     };
 
-    // The loads go out in the loop's order -- K, the next entries, V -- so
-    // that the loop is entered with the same loads in flight, in the same
-    // order, as it is re-entered from its back edge (the scheduling barriers
-    // keep the compiler from interleaving the groups).
-    phys = sanitize(load_entry(0));
-    issue_k(phys);
-    e_next = load_entry(1);
+    // The loads go out in the loop's order -- K, then V -- so that the loop
+    // is entered with the same loads in flight, in the same order, as it is
+    // re-entered from its back edge (the scheduling barriers keep the
+    // compiler from interleaving the groups).
+    ent = load_entries(0);
+    issue_k(0);
     __builtin_amdgcn_sched_barrier(0);
-    issue_v(phys);
+    issue_v(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma nounroll
     for (int r = 0; r < rounds - 1; ++r)
