@@ -1,27 +1,31 @@
 #!/usr/bin/env python3
 """Decode-step benchmark for paged KV-cache attention on one MI355X.
 
-One step = the cache write of each sequence's new token (pa_reshape_and_cache)
-followed by paged decode attention over every sequence's context
-(pa_decode_partitioned by default, pa_decode with --kernel single,
-pa_decode_cascade with --kernel cascade on a shared-prefix workload). The
-default workload is the Llama-8B-shaped GQA batch: 64 sequences, 32 query /
-8 KV heads, head size 128, bf16 KV, context lengths min(4096, 100 +
-floor(Exp(mean 400))), 16-token blocks scattered through a pool twice the size
-needed. Inputs are synthetic (seeded N(0, 1) values) and already resident in
-HBM when timing starts.
+One step = the cache write of each sequence's new token plus paged decode
+attention over every sequence's context. By default (--kernel pstep) both are
+one call, pa_decode_partitioned_step, which stores each new token's K/V in its
+slot and attends to it from registers (--kernel step: the same fused step on
+the balanced schedule, pa_decode_step); the other kernels (balanced,
+partitioned, single, cascade on a shared-prefix workload) run after a
+separate pa_reshape_and_cache call. The default workload is the Llama-8B-shaped GQA
+batch: 64 sequences, 32 query / 8 KV heads, head size 128, bf16 KV, context
+lengths min(4096, 100 + floor(Exp(mean 400))), 16-token blocks scattered
+through a pool twice the size needed. Inputs are synthetic (seeded N(0, 1)
+values) and already resident in HBM when timing starts.
 
 The KV working set of one step (~131 MB) fits in the 256 MB Infinity Cache, so
 consecutive steps rotate over R independent replicas of the batch (same
 lengths, different block placement and values; R * 131 MB >> 256 MB).
 
 Printed: one JSON line on stdout. `value` is KV-read GB/s of whole steps
-(scatter + attention, launch gaps included); `roofline` is the attention call
-alone, timed with HIP events on the launch stream (also after a 1 GiB write
-that evicts the caches: `attention_ms_cold_p50`); `stream_read` is the rate of the
-library's plain streaming-read kernel over 2 GiB, the achievable ceiling next to
-the nominal 8 TB/s; `cpu_baseline` is the fp64 oracle on the host cores (and on
-one thread) over a bounded sample of the same workload.
+(cache write + attention, launch gaps included, wall clock between two
+synchronisations); `roofline` is the attention call alone, timed with HIP
+events on the launch stream around a run of back-to-back calls (also after a
+1 GiB write that evicts the caches: `attention_ms_cold_p50`); `stream_read` is
+the rate of the library's plain streaming-read kernel over 2 GiB, the
+achievable ceiling next to the nominal 8 TB/s; `cpu_baseline` is the fp64
+oracle on the host cores (and on one thread) over a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -81,10 +85,11 @@ def main() -> int:
     ap.add_argument("--prefill-chunk", type=int, default=512,
                     help="--op prefill: query tokens per sequence (its last min(L, chunk) tokens)")
     ap.add_argument("--workload", default="llama8b_gqa_bf16")
-    ap.add_argument("--kernel", choices=("step", "balanced", "partitioned", "single", "cascade"),
-                    default="step",
-                    help="step: pa_decode_step, the cache write and the work-balanced attention in "
-                         "one call (default); balanced: pa_reshape_and_cache then "
+    ap.add_argument("--kernel", choices=("step", "pstep", "balanced", "partitioned", "single", "cascade"),
+                    default="pstep",
+                    help="pstep: pa_decode_partitioned_step, the cache write and the partitioned "
+                         "attention in one call (default); step: pa_decode_step, the same on the "
+                         "work-balanced schedule; balanced: pa_reshape_and_cache then "
                          "pa_decode_balanced; partitioned / single: pa_reshape_and_cache then "
                          "pa_decode_partitioned / pa_decode; cascade: pa_decode_cascade over the "
                          "prefix every table shares (shared-prefix workloads only)")
@@ -195,6 +200,10 @@ def main() -> int:
         if args.kernel == "step":
             pa.pa_decode_step(x["out"], w.query, x["new_key"], x["new_value"], w.key_cache,
                               w.value_cache, x["bt"], x["cl"], w.scale, x["ws"])
+        elif args.kernel == "pstep":
+            pa.pa_decode_partitioned_step(x["out"], w.query, x["new_key"], x["new_value"],
+                                          w.key_cache, w.value_cache, x["bt"], x["cl"], w.scale,
+                                          mcl, psize, x["ws"])
         elif args.kernel == "balanced":
             pa.pa_decode_balanced(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"],
                                   w.scale, x["ws"])
@@ -207,37 +216,43 @@ def main() -> int:
             pa.pa_decode_partitioned(x["out"], w.query, w.key_cache, w.value_cache, x["bt"], x["cl"],
                                      w.scale, mcl, psize, x["ws"])
 
-    def step(i, ev=None):
+    def step(i):
         x = inputs[i % len(inputs)]
         w = x["w"]
-        if args.kernel != "step":
+        if args.kernel not in ("step", "pstep"):
             pa.pa_reshape_and_cache(w.key, w.value, w.key_cache, w.value_cache, x["slots"])
         elif x["early_slots"].numel():
             # several new tokens per sequence: all but the last go through the cache write
             pa.pa_reshape_and_cache(x["early_key"], x["early_value"], w.key_cache, w.value_cache,
                                     x["early_slots"])
-        if ev is not None:
-            ev[0].record()
         attention(x)
-        if ev is not None:
-            ev[1].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    # Timed region: exactly K steps between two synchronisations.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # Timed region: exactly K steps between two synchronisations, nothing else
+    # on the stream (event records would add their own gaps).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
     log(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    # Duration of the attention call alone: the same K calls again, back to
+    # back on the stream they run on, between two HIP events (an event pair
+    # per call would add its own gap to every call).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        attention(inputs[i % len(inputs)])
+    e1.record()
+    torch.cuda.synchronize()
+    call_ms = np.array([e0.elapsed_time(e1) / args.steps])
 
     cold_ms = None
     if args.cold_calls > 0:
@@ -283,13 +298,15 @@ def main() -> int:
             "max_context_len": mcl, "kv_bytes_per_step": kv_bytes,
             "kernel": {"single": "pa_decode", "partitioned": "pa_decode_partitioned",
                        "cascade": "pa_decode_cascade", "balanced": "pa_decode_balanced",
-                       "step": "pa_decode_step"}[args.kernel],
-            "partition_size": psize if args.kernel in ("partitioned", "cascade") else None,
+                       "step": "pa_decode_step",
+                       "pstep": "pa_decode_partitioned_step"}[args.kernel],
+            "partition_size": psize if args.kernel in ("partitioned", "cascade", "pstep") else None,
             "unique_kv_bytes_per_step": unique_bytes,
             "prefix_blocks": npb or None,
             "replicas": args.replicas, "pool_blocks": base.num_blocks,
-            "step": "pa_decode_step (cache write fused into the attention call)"
-                    if args.kernel == "step" else "pa_reshape_and_cache + attention",
+            "step": f"{'pa_decode_step' if args.kernel == 'step' else 'pa_decode_partitioned_step'} "
+                    "(cache write fused into the attention call)"
+                    if args.kernel in ("step", "pstep") else "pa_reshape_and_cache + attention",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(S / (ms_per_step * 1e-3), 1),
@@ -305,6 +322,8 @@ def main() -> int:
             "traffic": traffic,
             "kernel": {"step": "attention call: paged_decode_balanced_kernel (cache write "
                                "fused) + balanced_reduce_kernel",
+                       "pstep": "attention call: paged_decode_persistent_kernel (cache write "
+                                "fused) + lse_reduce_kernel",
                        "balanced": "attention call: paged_decode_balanced_kernel + "
                                    "balanced_reduce_kernel",
                        "single": "paged_decode_kernel",
@@ -312,8 +331,9 @@ def main() -> int:
                                       "lse_reduce_kernel",
                        "cascade": "attention call: cascade_prefix_kernel + "
                                   "paged_decode_persistent_kernel + lse_reduce_kernel"}[args.kernel],
-            "timing": "HIP events around each attention call on its launch stream, mean over "
-                      "the timed steps",
+            "timing": "HIP events on the launch stream around the timed number of attention "
+                      "calls issued back to back (no cache write between them), divided by that "
+                      "number",
         },
         "cpu_baseline": None,
     }

@@ -21,6 +21,8 @@
  *                          byte ranges over the whole batch
  *   pa_decode_step         cache write of each sequence's new token plus
  *                          balanced decode, in one call
+ *   pa_decode_partitioned_step
+ *                          the same step on the partitioned schedule
  *   pa_decode_cascade      the same result for a batch whose tables all begin
  *                          with the same physical blocks (a shared prefix):
  *                          the prefix is read once per KV head for the whole
@@ -361,6 +363,37 @@ pa_status_t pa_decode_step(void* out, pa_dtype_t out_dtype, const void* query, c
                            const int32_t* context_lens, int num_seqs, int num_q_heads,
                            int num_kv_heads, int head_size, int block_size, int64_t num_blocks,
                            float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_partitioned_step -- the same decode step (write each sequence's
+ * new token into the cache and attend over the context that includes it) on
+ * the partitioned schedule of pa_decode_partitioned.
+ *
+ * The write is that of pa_decode_step: key[s][h][:] and value[s][h][:] go to
+ * row (L - 1) % 16 of block block_tables[s][(L - 1) / 16] of both pools for
+ * every sequence with L = context_lens[s] >= 1 whose context is readable and
+ * whose entry for position L - 1 lies in [0, NB). out is the attention of
+ * pa_decode_partitioned over the L tokens, the new one taken from key/value
+ * directly (by the partition that holds position L - 1; the pools are read
+ * only below it). Same result as pa_reshape_and_cache followed by
+ * pa_decode_partitioned up to fp32 rounding order.
+ *
+ *   key, value  [S][Hkv][D] of kv_dtype (device), 16-byte aligned.
+ *   key_cache, value_cache  updated in place (one slot per sequence).
+ * The block holding position L - 1 must not be shared with another sequence
+ * in the call. Workspace, partition size and every other argument, check and
+ * error as pa_decode_partitioned; key or value null with num_seqs > 0 is
+ * PA_EINVAL.
+ */
+pa_status_t pa_decode_partitioned_step(void* out, pa_dtype_t out_dtype, const void* query,
+                                       const void* key, const void* value, void* key_cache,
+                                       void* value_cache, pa_dtype_t kv_dtype,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, int num_seqs,
+                                       int num_q_heads, int num_kv_heads, int head_size,
+                                       int block_size, int64_t num_blocks, float scale,
+                                       int max_context_len, int partition_size, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes pa_decode_cascade needs. With

@@ -20,6 +20,7 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOSPACE = 0, 1, 2
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode", "pa_decode_partitioned",
            "pa_decode_partitioned_workspace_size", "pa_decode_partitioned_noalloc",
            "pa_decode_balanced", "pa_decode_balanced_workspace_size", "pa_decode_step",
+           "pa_decode_partitioned_step",
            "pa_decode_cascade",
            "pa_decode_cascade_workspace_size", "pa_prefill", "pa_stream_read", "pa_status_str",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token",
@@ -66,6 +67,9 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_step.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32,
                                    i32, i64, f32, vp, sz, vp]
     lib.pa_decode_step.restype = i32
+    lib.pa_decode_partitioned_step.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, vp, i32, i32,
+                                               i32, i32, i32, i64, f32, i32, i32, vp, sz, vp]
+    lib.pa_decode_partitioned_step.restype = i32
     lib.pa_decode_balanced_workspace_size.argtypes = [i32, i32, i32]
     lib.pa_decode_balanced_workspace_size.restype = sz
     lib.pa_decode_partitioned_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, i32, i32,
@@ -344,6 +348,37 @@ def pa_decode_balanced(out: torch.Tensor, query: torch.Tensor, key_cache: torch.
     return out
 
 
+def _step_inputs(key, value, key_cache, value_cache, S, Hkv, D, workspace):
+    _dev(key, value, workspace)
+    if key.shape != (S, Hkv, D) or value.shape != key.shape:
+        raise ValueError("key and value must be [S, Hkv, D]")
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype:
+        raise TypeError("key, value and caches must share one dtype")
+
+
+def pa_decode_partitioned_step(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor,
+                               value: torch.Tensor, key_cache: torch.Tensor,
+                               value_cache: torch.Tensor, block_tables: torch.Tensor,
+                               context_lens: torch.Tensor, scale: float, max_context_len: int,
+                               partition_size: int, workspace: torch.Tensor,
+                               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """One decode step on the partitioned schedule: key/value [S, Hkv, D] (each sequence's
+    new token) are written at position context_lens[s] - 1 through the block table, and out
+    is the attention over the whole context, new token included. workspace as for
+    pa_decode_partitioned (decode_workspace() makes one)."""
+    S, Hq, Hkv, D, B, NB, MB = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                              context_lens)
+    _step_inputs(key, value, key_cache, value_cache, S, Hkv, D, workspace)
+    rc = load().pa_decode_partitioned_step(
+        out.data_ptr(), _dtype_code(out.dtype), query.data_ptr(), key.data_ptr(), value.data_ptr(),
+        key_cache.data_ptr(), value_cache.data_ptr(), _dtype_code(key_cache.dtype),
+        block_tables.data_ptr(), MB, context_lens.data_ptr(), S, Hq, Hkv, D, B, NB, float(scale),
+        int(max_context_len), int(partition_size), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(query, stream))
+    _check(rc, "pa_decode_partitioned_step")
+    return out
+
+
 def pa_decode_step(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                    key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
                    context_lens: torch.Tensor, scale: float, workspace: torch.Tensor,
@@ -353,11 +388,7 @@ def pa_decode_step(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, va
     whole context, new token included."""
     S, Hq, Hkv, D, B, NB, MB = _decode_common(out, query, key_cache, value_cache, block_tables,
                                               context_lens)
-    _dev(key, value, workspace)
-    if key.shape != (S, Hkv, D) or value.shape != key.shape:
-        raise ValueError("key and value must be [S, Hkv, D]")
-    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype:
-        raise TypeError("key, value and caches must share one dtype")
+    _step_inputs(key, value, key_cache, value_cache, S, Hkv, D, workspace)
     rc = load().pa_decode_step(out.data_ptr(), _dtype_code(out.dtype), query.data_ptr(),
                                key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
                                value_cache.data_ptr(), _dtype_code(key_cache.dtype),

@@ -293,14 +293,17 @@ size_t pa_decode_partitioned_workspace_size(int num_seqs, int num_q_heads, int h
     return 2 * align256(r * sizeof(float)) + align256(r * sizeof(float) * head_size);
 }
 
-pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* query,
-                                  const void* key_cache, const void* value_cache,
-                                  pa_dtype_t kv_dtype, const int32_t* block_tables,
-                                  int max_blocks_per_seq, const int32_t* context_lens,
-                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
-                                  int block_size, int64_t num_blocks, float scale,
-                                  int max_context_len, int partition_size, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+// Shared by pa_decode_partitioned and pa_decode_partitioned_step (new_key =
+// nullptr: no write).
+static pa_status_t decode_partitioned(void* out, pa_dtype_t out_dtype, const void* query,
+                                      const void* new_key, const void* new_value,
+                                      const void* key_cache, const void* value_cache,
+                                      pa_dtype_t kv_dtype, const int32_t* block_tables,
+                                      int max_blocks_per_seq, const int32_t* context_lens,
+                                      int num_seqs, int num_q_heads, int num_kv_heads,
+                                      int head_size, int block_size, int64_t num_blocks,
+                                      float scale, int max_context_len, int partition_size,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
     pa_status_t st = check_decode(out, out_dtype, query, key_cache, value_cache, kv_dtype,
                                   block_tables, max_blocks_per_seq, context_lens, num_seqs,
                                   num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
@@ -309,6 +312,10 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
         return st;
     if (max_context_len < 0 || partition_size <= 0 || partition_size % pa::kBlockSize != 0)
         return PA_EINVAL;
+    if (new_key != nullptr || new_value != nullptr) {
+        if (!new_key || !new_value || !aligned(new_key, 16) || !aligned(new_value, 16))
+            return PA_EINVAL;
+    }
     const int np = num_partitions(max_context_len, partition_size);
     if (np > kMaxGridYZ)
         return PA_EUNSUPPORTED;
@@ -338,6 +345,8 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
     p.table_blocks = max_blocks_per_seq;
     p.num_seqs = num_seqs;
     p.persistent = num_seqs <= pa::kMaxPersistentSeqs && num_kv_heads <= pa::kMaxPersistentKvHeads;
+    p.new_key = new_key;
+    p.new_value = new_value;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int waves = choose_waves(p.partition_blocks, elem_bytes(kv_dtype), head_size, p.group,
                                    pa::kPartWaves);
@@ -364,6 +373,37 @@ pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* q
     r.partition_blocks = p.partition_blocks;
     r.table_blocks = max_blocks_per_seq;
     return from_hip(pa::launch_reduce(r, head_size, out_dtype == PA_BF16, num_seqs, s));
+}
+
+pa_status_t pa_decode_partitioned(void* out, pa_dtype_t out_dtype, const void* query,
+                                  const void* key_cache, const void* value_cache,
+                                  pa_dtype_t kv_dtype, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
+                                  int block_size, int64_t num_blocks, float scale,
+                                  int max_context_len, int partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    return decode_partitioned(out, out_dtype, query, nullptr, nullptr, key_cache, value_cache,
+                              kv_dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_size, block_size, num_blocks, scale,
+                              max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_decode_partitioned_step(void* out, pa_dtype_t out_dtype, const void* query,
+                                       const void* key, const void* value, void* key_cache,
+                                       void* value_cache, pa_dtype_t kv_dtype,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, int num_seqs,
+                                       int num_q_heads, int num_kv_heads, int head_size,
+                                       int block_size, int64_t num_blocks, float scale,
+                                       int max_context_len, int partition_size, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && (!key || !value))
+        return PA_EINVAL;
+    return decode_partitioned(out, out_dtype, query, key, value, key_cache, value_cache, kv_dtype,
+                              block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                              num_kv_heads, head_size, block_size, num_blocks, scale,
+                              max_context_len, partition_size, workspace, workspace_bytes, stream);
 }
 
 // Workspace of the balanced decode: descriptors, then the partials of the at

@@ -53,27 +53,49 @@ __device__ __forceinline__ void fill_rows(const DecodeParams& p, int kvh, int s,
 // tokens, readable), computed by the whole workgroup. With `direct` the range
 // is the whole context and the output row is written; otherwise the range's
 // (max, sum, normalised output) go to partial slot `slot` of the workspace.
-// All arguments are wave-uniform.
-template <typename KV, int D, int GMAX, typename OUT>
+// With WRITE, the range that holds the context's last token (its new one)
+// streams only the tokens before it from the pool; wave 0 takes the new
+// token's K and V from p.new_key / p.new_value, attends to it and stores it
+// in its slot, so the attention never reads the slot being written. All
+// arguments are wave-uniform.
+template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 __device__ __forceinline__ void process_range(const DecodeParams& p, float* smem, int kvh, int s,
                                               int L, int pb0, int pb1, int slot, bool direct) {
     using Gm = Geometry<KV, D>;
-    constexpr int CH = Gm::kCh, EPC = Gm::kEpc;
+    constexpr int CH = Gm::kCh, EPC = Gm::kEpc, ROW = Gm::kRow;
     constexpr int BPW = decode_bpw(KV::kBytes, D, GMAX);
     constexpr int GP = decode_pstride(GMAX);
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nw = blockDim.x / kWave;
     const int per_round = nw * BPW;
-    const int rounds = (pb1 - pb0 + per_round - 1) / per_round;
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool with_new = WRITE && pb1 * kBlockSize >= L;      // the range holds token L - 1
+    const int L_pool = with_new ? L - 1 : L;
+    const int pb1_pool = min(pb1, (L_pool + kBlockSize - 1) / kBlockSize);
+    const int rounds = (pb1_pool - pb0 + per_round - 1) / per_round;
     u32x4 qa[Gm::kNq];
     load_query<KV, D>(p, kvh, s, qa);
+    NewToken<KV, D> tok;
+    if constexpr (WRITE) {
+        if (with_new && wave == 0) {
+            const int64_t src = ((int64_t)s * p.num_kv_heads + kvh) * ROW;
+            tok = load_new_token<KV, D>(static_cast<const char*>(p.new_key) + src,
+                                        static_cast<const char*>(p.new_value) + src);
+        }
+    }
     WaveAcc<KV, D, GMAX> acc;
     acc.reset();
-    accumulate_blocks<KV, D, GMAX>(p, smem + wave * (BPW * kBlockSize * GP), qa, kvh, s, L, pb1,
-                                   pb0 + wave * BPW, per_round, rounds, acc);
+    if (rounds > 0)
+        accumulate_blocks<KV, D, GMAX>(p, smem + wave * (BPW * kBlockSize * GP), qa, kvh, s, L_pool,
+                                       pb1_pool, pb0 + wave * BPW, per_round, rounds, acc);
+    if constexpr (WRITE) {
+        if (with_new && wave == 0) {
+            accumulate_token<KV, D, GMAX>(p, qa, tok, acc);
+            store_new_token<KV, D>(p, tok, s, kvh, L, p.skip_blocks);
+        }
+    }
 
-    const int lane = threadIdx.x & (kWave - 1);
     const int Hq = p.num_q_heads, G = p.group;
     const int g = lane >> 4;       // MFMA lane group: output rows 4g..4g+3
     const int r16 = lane & 15;
@@ -148,7 +170,7 @@ __device__ __forceinline__ int schedule_blocks(int L, const DecodeParams& p) {
 }
 
 // Partition `part` of the context of KV head `kvh` of sequence `s`.
-template <typename KV, int D, int GMAX, typename OUT>
+template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 __device__ __forceinline__ void process_partition(const DecodeParams& p, float* smem, int kvh,
                                                   int s, int L, int part) {
     const bool bad = context_unreadable(L, p.table_blocks, p.num_partitions, p.partition_blocks,
@@ -163,18 +185,18 @@ __device__ __forceinline__ void process_partition(const DecodeParams& p, float* 
     const int np = (nblk + PB - 1) / PB;
     if (part >= np)
         return;
-    process_range<KV, D, GMAX, OUT>(p, smem, kvh, s, L, part * PB, min((part + 1) * PB, nblk), part,
-                                    np == 1 && !p.partials_only);
+    process_range<KV, D, GMAX, OUT, WRITE>(p, smem, kvh, s, L, part * PB, min((part + 1) * PB, nblk),
+                                           part, np == 1 && !p.partials_only);
 }
 
 // Grid schedule: one workgroup per (KV head, sequence, partition). The single
 // pass is the case of one partition spanning the whole table.
-template <typename KV, int D, int GMAX, typename OUT>
+template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeParams p) {
     extern __shared__ float smem[];
-    process_partition<KV, D, GMAX, OUT>(p, smem, blockIdx.x, blockIdx.y,
-                                        call_len(p.context_lens[blockIdx.y], p.skip_blocks),
-                                        blockIdx.z);
+    process_partition<KV, D, GMAX, OUT, WRITE>(p, smem, blockIdx.x, blockIdx.y,
+                                               call_len(p.context_lens[blockIdx.y], p.skip_blocks),
+                                               blockIdx.z);
 }
 
 // Waves per SIMD the persistent kernel is register-allocated for: three 4-wave
@@ -192,7 +214,7 @@ constexpr int persistent_waves_per_simd() {
 // neighbouring workgroups read the same physical blocks for different KV
 // heads at about the same time (measured faster on MI355X than contiguous,
 // tile-balanced ranges, and than dealing KV head by KV head).
-template <typename KV, int D, int GMAX, typename OUT>
+template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 __global__ __launch_bounds__(kPartWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(persistent_waves_per_simd<KV, D, GMAX>())))
 void paged_decode_persistent_kernel(DecodeParams p) {
@@ -255,7 +277,7 @@ void paged_decode_persistent_kernel(DecodeParams p) {
             if (seq < 0)
                 break;
             const int pk = __builtin_amdgcn_readfirstlane(list[2 * k + 1]);
-            process_partition<KV, D, GMAX, OUT>(p, smem, pk & 0xFF, seq,
+            process_partition<KV, D, GMAX, OUT, WRITE>(p, smem, pk & 0xFF, seq,
                                                 __builtin_amdgcn_readfirstlane(lens[seq]), pk >> 8);
             __syncthreads();                        // the item's LDS is free again
         }
@@ -382,22 +404,22 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams
     }
 }
 
-template <typename KV, int D, int GMAX, typename OUT>
+template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 hipError_t launch_decode_grid(const DecodeParams& p, int num_seqs, int grid_partitions, int waves,
                               hipStream_t stream) {
     const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, waves);
-    hipLaunchKernelGGL((paged_decode_kernel<KV, D, GMAX, OUT>),
+    hipLaunchKernelGGL((paged_decode_kernel<KV, D, GMAX, OUT, WRITE>),
                        dim3(p.num_kv_heads, num_seqs, grid_partitions), dim3(waves * kWave), lds,
                        stream, p);
     return hipGetLastError();
 }
 
-template <typename KV, int D, int GMAX, typename OUT>
-hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, int grid_partitions, int waves,
+template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
+hipError_t launch_decode_w(const DecodeParams& p, int num_seqs, int grid_partitions, int waves,
                            hipStream_t stream) {
     if (!p.persistent)
-        return launch_decode_grid<KV, D, GMAX, OUT>(p, num_seqs, grid_partitions, waves, stream);
-    const auto kernel = paged_decode_persistent_kernel<KV, D, GMAX, OUT>;
+        return launch_decode_grid<KV, D, GMAX, OUT, WRITE>(p, num_seqs, grid_partitions, waves, stream);
+    const auto kernel = paged_decode_persistent_kernel<KV, D, GMAX, OUT, WRITE>;
     // Persistent: as many workgroups as the GPU keeps resident at once (never
     // more than there can be items).
     const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, waves) + persistent_lds_bytes(num_seqs);
@@ -411,7 +433,7 @@ hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, int grid_partiti
         // per (KV head, sequence, partition) computes the same partials.
         DecodeParams g = p;
         g.persistent = 0;
-        return launch_decode_grid<KV, D, GMAX, OUT>(g, num_seqs, grid_partitions, waves, stream);
+        return launch_decode_grid<KV, D, GMAX, OUT, WRITE>(g, num_seqs, grid_partitions, waves, stream);
     }
     e = resident_workgroups_per_cu(dev, reinterpret_cast<const void*>(kernel), waves * kWave, lds,
                                    &per_cu);
@@ -422,6 +444,13 @@ hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, int grid_partiti
                                                                          std::max(per_cu, 1)));
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(waves * kWave), lds, stream, p);
     return hipGetLastError();
+}
+
+template <typename KV, int D, int GMAX, typename OUT>
+hipError_t launch_decode_t(const DecodeParams& p, int num_seqs, int grid_partitions, int waves,
+                           hipStream_t stream) {
+    return p.new_key ? launch_decode_w<KV, D, GMAX, OUT, true>(p, num_seqs, grid_partitions, waves, stream)
+                     : launch_decode_w<KV, D, GMAX, OUT, false>(p, num_seqs, grid_partitions, waves, stream);
 }
 
 template <typename KV, int D, typename OUT>

@@ -222,12 +222,21 @@ void paged_decode_balanced_kernel(BalancedParams bp) {
         } else {
             u32x4 qa[Gm::kNq];
             load_query<KV, D>(p, kvh, s, qa);
-            WaveAcc<KV, D, GMAX> acc;
-            acc.reset();
             // With the write fused, the segment that ends the row streams only
             // the tokens before the new one; the new token's K and V come from
-            // the inputs (the slot being written is never read).
+            // the inputs (the slot being written is never read), loaded before
+            // the blocks are streamed.
             const bool with_new = WRITE && j1 == nb;
+            NewToken<KV, D> tok;
+            if constexpr (WRITE) {
+                if (with_new) {
+                    const int64_t src = ((int64_t)s * Hkv + kvh) * ROW;
+                    tok = load_new_token<KV, D>(static_cast<const char*>(bp.new_key) + src,
+                                                static_cast<const char*>(bp.new_value) + src);
+                }
+            }
+            WaveAcc<KV, D, GMAX> acc;
+            acc.reset();
             const int L_old = with_new ? L - 1 : L;
             const int pb1 = min(j1, (L_old + kBlockSize - 1) / kBlockSize);
             if (pb1 > j0)
@@ -235,22 +244,8 @@ void paged_decode_balanced_kernel(BalancedParams bp) {
                                                (pb1 - j0 + BPW - 1) / BPW, acc);
             if constexpr (WRITE) {
                 if (with_new) {
-                    const int64_t src = ((int64_t)s * Hkv + kvh) * ROW;
-                    const char* k_row = static_cast<const char*>(bp.new_key) + src;
-                    const char* v_row = static_cast<const char*>(bp.new_value) + src;
-                    accumulate_token<KV, D, GMAX>(p, qa, k_row, v_row, acc);
-                    // Store the new token's K and V rows in their slot (when the
-                    // table entry lies inside the pool).
-                    const int tb = (L - 1) / kBlockSize, tr = (L - 1) % kBlockSize;
-                    const int phys = p.block_tables[(int64_t)s * p.max_blocks_per_seq + tb];
-                    if (phys >= 0 && static_cast<int64_t>(phys) < p.num_blocks && lane < 2 * CH) {
-                        const bool is_v = lane >= CH;
-                        const int c = is_v ? lane - CH : lane;
-                        const u32x4 x = ld16((is_v ? v_row : k_row) + c * 16);
-                        char* dst = static_cast<char*>(const_cast<void*>(is_v ? p.v_cache : p.k_cache)) +
-                                    (((int64_t)phys * Hkv + kvh) * kBlockSize + tr) * ROW + c * 16;
-                        *reinterpret_cast<u32x4*>(dst) = x;
-                    }
+                    accumulate_token<KV, D, GMAX>(p, qa, tok, acc);
+                    store_new_token<KV, D>(p, tok, s, kvh, L, 0);
                 }
             }
             float srow[4];

@@ -399,30 +399,54 @@ __device__ __forceinline__ void accumulate_blocks(const DecodeParams& p, float* 
     round(rounds - 1, std::false_type{});
 }
 
-// One more token, given by its K and V rows (D elements each, in global
-// memory) instead of through the pool: the same online-softmax step as a
-// round, with the token in column 0 of the MFMA tile and every other column
-// masked. Used for the step's new token when the call also writes it, so that
-// the attention never reads the slot being written.
+// The step's new token of one (sequence, KV head), loaded into one register
+// before the blocks are streamed (so its load latency hides under theirs):
+// lane l < CH holds 16-byte chunk l of the K row, lane CH <= l < 2 CH chunk
+// l - CH of the V row -- the layout its store into the slot takes.
+template <typename KV, int D>
+struct NewToken {
+    u32x4 row;
+};
+
+template <typename KV, int D>
+__device__ __forceinline__ NewToken<KV, D> load_new_token(const char* k_row, const char* v_row) {
+    constexpr int CH = Geometry<KV, D>::kCh;
+    const int lane = threadIdx.x & (kWave - 1);
+    NewToken<KV, D> t;
+    t.row = lane < CH       ? ld16(k_row + lane * 16)
+            : lane < 2 * CH ? ld16(v_row + (lane - CH) * 16)
+                            : u32x4{0u, 0u, 0u, 0u};
+    return t;
+}
+
+__device__ __forceinline__ u32x4 shfl16(const u32x4& x, int src) {
+    return u32x4{static_cast<uint32_t>(__shfl(static_cast<int>(x[0]), src, kWave)),
+                 static_cast<uint32_t>(__shfl(static_cast<int>(x[1]), src, kWave)),
+                 static_cast<uint32_t>(__shfl(static_cast<int>(x[2]), src, kWave)),
+                 static_cast<uint32_t>(__shfl(static_cast<int>(x[3]), src, kWave))};
+}
+
+// One more token, the new one: the same online-softmax step as a round, with
+// the token in column 0 of the MFMA tile and every other column masked. The
+// attention thus never reads the slot the call writes.
 template <typename KV, int D, int GMAX>
 __device__ __forceinline__ void accumulate_token(const DecodeParams& p,
                                                  const u32x4 (&qa)[Geometry<KV, D>::kNq],
-                                                 const char* k_row, const char* v_row,
+                                                 const NewToken<KV, D>& t,
                                                  WaveAcc<KV, D, GMAX>& acc) {
     using Gm = Geometry<KV, D>;
     using Op = Ops<KV>;
     constexpr int NQ = Gm::kNq, CH = Gm::kCh, EPC = Gm::kEpc;
     const int lane = threadIdx.x & (kWave - 1);
     const int g = lane >> 4, r16 = lane & 15;
-    u32x4 kn[NQ];
-#pragma unroll
-    for (int c = 0; c < NQ; ++c)
-        kn[c] = r16 == 0 ? ld16(k_row + (g + 4 * c) * 16) : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 vn = lane < CH ? ld16(v_row + lane * 16) : u32x4{0u, 0u, 0u, 0u};
+    // K as token column 0 of the MFMA B operand: lanes 16g take chunks g + 4c.
     f32x4 lg = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int c = 0; c < NQ; ++c)
-        lg = Op::qk(qa[c], kn[c], lg);
+    for (int c = 0; c < NQ; ++c) {
+        const u32x4 kc = shfl16(t.row, g + 4 * c);
+        lg = Op::qk(qa[c], r16 == 0 ? kc : u32x4{0u, 0u, 0u, 0u}, lg);
+    }
+    const u32x4 vn = shfl16(t.row, lane < CH ? CH + lane : 0);
     float pn[4], alpha[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -442,6 +466,26 @@ __device__ __forceinline__ void accumulate_token(const DecodeParams& p,
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
             acc.o[h][e] = fmaf(ph, vf[e], acc.o[h][e] * al);
+    }
+}
+
+// Stores the new token's K and V rows at position L - 1 of sequence s (table
+// entry skip + (L - 1) / 16), KV head kvh, when that entry lies inside the
+// pool (otherwise the row's output is NaN already and nothing is written).
+template <typename KV, int D>
+__device__ __forceinline__ void store_new_token(const DecodeParams& p, const NewToken<KV, D>& t,
+                                                int s, int kvh, int L, int skip) {
+    using Gm = Geometry<KV, D>;
+    constexpr int CH = Gm::kCh, ROW = Gm::kRow;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int tb = (L - 1) / kBlockSize, tr = (L - 1) % kBlockSize;
+    const int phys = p.block_tables[(int64_t)s * p.max_blocks_per_seq + skip + tb];
+    if (phys >= 0 && static_cast<int64_t>(phys) < p.num_blocks && lane < 2 * CH) {
+        const bool is_v = lane >= CH;
+        const int c = is_v ? lane - CH : lane;
+        char* dst = static_cast<char*>(const_cast<void*>(is_v ? p.v_cache : p.k_cache)) +
+                    (((int64_t)phys * p.num_kv_heads + kvh) * kBlockSize + tr) * ROW + c * 16;
+        *reinterpret_cast<u32x4*>(dst) = t.row;
     }
 }
 

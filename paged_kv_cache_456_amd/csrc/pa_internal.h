@@ -51,6 +51,8 @@ struct DecodeParams {
     int table_blocks;              // max_blocks_per_seq - skip_blocks
     int partials_only;             // 1: write partials for every partition, never `out`
     float scale_log2;              // scale * log2(e)
+    const void* new_key;           // [S][Hkv][D]: each sequence's new token, stored at position
+    const void* new_value;         //   L - 1 and attended from here (nullptr: no write)
 };
 
 struct ReduceParams {

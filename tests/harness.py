@@ -195,3 +195,37 @@ def gpu_balanced(w: Workload, step: bool = False, out_dtype=torch.float32, in_pl
                           bt, cl, w.scale, ws)
     torch.cuda.synchronize()
     return GpuResult(out, kc, vc, ws)
+
+
+def gpu_pstep(w: Workload, partition_size: Optional[int] = None, out_dtype=torch.float32,
+              in_place: bool = False, block_tables: Optional[torch.Tensor] = None,
+              context_lens: Optional[torch.Tensor] = None,
+              max_context_len: Optional[int] = None) -> GpuResult:
+    """The step on the GPU through pa_decode_partitioned_step (partition size from the
+    workload's spec unless given): each sequence's last new token is written and attended by
+    the call itself; earlier new tokens of a sequence, when it has several, go through
+    pa_reshape_and_cache first."""
+    bt, cl, slots = device_inputs(w)
+    if block_tables is not None:
+        bt = block_tables
+    if context_lens is not None:
+        cl = context_lens
+    kc = w.key_cache if in_place else w.key_cache.clone()
+    vc = w.value_cache if in_place else w.value_cache.clone()
+    S, Hq, D = w.query.shape
+    psize = w.spec.partition_size if partition_size is None else partition_size
+    mcl = w.max_context_len if max_context_len is None else max_context_len
+    out = torch.empty((S, Hq, D), dtype=out_dtype, device=kc.device)
+    ws = pa.decode_workspace(S, Hq, D, mcl, psize, device=kc.device)
+    ws.fill_(0xFF)                      # NaN bit patterns: the call must not depend on them
+    per = w.spec.new_tokens_per_seq
+    idx = torch.arange(S, device=kc.device) * per + (per - 1)
+    if per > 1:
+        keep = torch.ones(S * per, dtype=torch.bool, device=kc.device)
+        keep[idx] = False
+        pa.pa_reshape_and_cache(w.key[keep].contiguous(), w.value[keep].contiguous(), kc, vc,
+                                slots[keep].contiguous())
+    pa.pa_decode_partitioned_step(out, w.query, w.key[idx].contiguous(), w.value[idx].contiguous(),
+                                  kc, vc, bt, cl, w.scale, mcl, psize, ws)
+    torch.cuda.synchronize()
+    return GpuResult(out, kc, vc, ws)

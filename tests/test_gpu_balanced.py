@@ -73,30 +73,38 @@ def test_shape_matrix(dtype, D, Hkv, G, mode):
     _report(f"{dtype} D={D} Hkv={Hkv} G={G} {mode}", max_abs_err(g.out, r.out), TOL[dtype])
 
 
+# Head counts for the edge cases: two and four KV heads (rows of several
+# sequences and heads share a workgroup's range either way).
+HKV = [2, 4]
+
+
 @pytest.mark.parametrize("mode", MODES)
-def test_mixed_lengths(mode):
+@pytest.mark.parametrize("hkv", HKV)
+def test_mixed_lengths(hkv, mode):
     """One long context among short ones, a single sequence, many one-token contexts: the
     cut points fall everywhere (inside rows, between waves, between workgroups)."""
     for lengths in ([8000, 3, 40, 1, 700], [20000], [1, 2, 3], [4096] * 3 + [1] * 40,
                     [16, 17, 32, 33] * 30, [300000 // 16] * 2):
-        spec = wl.custom_spec(lengths, 8, 2, 128, torch.bfloat16, index=410 + len(lengths))
+        spec = wl.custom_spec(lengths, 4 * hkv, hkv, 128, torch.bfloat16,
+                              index=410 + len(lengths) + hkv)
         w = wl.make_workload(spec, device="cuda")
         r = oracle_step(w)
         g = gpu_balanced(w, step=mode == "step")
         check_scatter(w, g, r)
-        _report(f"mixed {lengths[:4]} {mode}", max_abs_err(g.out, r.out), TOL[torch.bfloat16])
+        _report(f"mixed {lengths[:4]} Hkv={hkv} {mode}", max_abs_err(g.out, r.out),
+                TOL[torch.bfloat16])
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("S,G", [(4096, 16), (4096, 4)])
-def test_sequence_cap(S, G, mode):
+@pytest.mark.parametrize("S,G,hkv", [(4096, 16, 2), (4096, 4, 2), (4096, 4, 4)])
+def test_sequence_cap(S, G, hkv, mode):
     lengths = np.random.default_rng(S + G + 7).integers(1, 49, S).tolist()
-    spec = wl.custom_spec(lengths, 2 * G, 2, 128, torch.bfloat16, index=440 + G)
+    spec = wl.custom_spec(lengths, hkv * G, hkv, 128, torch.bfloat16, index=440 + G + hkv)
     w = wl.make_workload(spec, device="cuda")
     r = oracle_step(w)
     g = gpu_balanced(w, step=mode == "step")
     check_scatter(w, g, r)
-    _report(f"S={S} G={G} {mode}", max_abs_err(g.out, r.out), TOL[torch.bfloat16])
+    _report(f"S={S} G={G} Hkv={hkv} {mode}", max_abs_err(g.out, r.out), TOL[torch.bfloat16])
 
 
 def test_sequence_cap_exceeded():
@@ -107,10 +115,12 @@ def test_sequence_cap_exceeded():
 
 
 @pytest.mark.parametrize("mode", MODES)
-def test_edge_lengths_and_bad_tables(mode):
+@pytest.mark.parametrize("hkv", HKV)
+def test_edge_lengths_and_bad_tables(hkv, mode):
     """Empty contexts give a zero row (and the step writes nothing for them); a context
     longer than its table, or one reaching a block outside the pool, gives a NaN row."""
-    spec = wl.custom_spec([0, 1, 40, 33, 20, 0, 5], 8, 2, 64, torch.bfloat16, index=450)
+    spec = wl.custom_spec([0, 1, 40, 33, 20, 0, 5], 4 * hkv, hkv, 64, torch.bfloat16,
+                          index=450 + hkv)
     w = wl.make_workload(spec, device="cuda", table_pad=-1)
     r = oracle_step(w, seqs=[0, 1, 2, 5, 6])
     bt, cl, _ = device_inputs(w)
@@ -120,7 +130,7 @@ def test_edge_lengths_and_bad_tables(mode):
     cl_bad[4] = bt.shape[1] * 16 + 1           # longer than its table
     g = gpu_balanced(w, step=mode == "step", block_tables=bt_bad, context_lens=cl_bad)
     ok = torch.as_tensor([0, 1, 2, 5, 6], device="cuda")
-    _report(f"edge {mode}", max_abs_err(g.out[ok], r.out), TOL[torch.bfloat16])
+    _report(f"edge Hkv={hkv} {mode}", max_abs_err(g.out[ok], r.out), TOL[torch.bfloat16])
     assert torch.equal(g.out[0], torch.zeros_like(g.out[0]))
     assert torch.equal(g.out[5], torch.zeros_like(g.out[5]))
     assert torch.isnan(g.out[3]).all() and torch.isnan(g.out[4]).all()
@@ -183,9 +193,10 @@ def test_step_matches_separate_write_and_decode():
 
 
 @pytest.mark.parametrize("mode", MODES)
-def test_single_token_returns_v_exactly(mode):
+@pytest.mark.parametrize("hkv", HKV)
+def test_single_token_returns_v_exactly(hkv, mode):
     for dtype in (torch.float32, torch.bfloat16):
-        spec = wl.custom_spec([1, 1, 1], 8, 2, 128, dtype, index=303)
+        spec = wl.custom_spec([1, 1, 1], 4 * hkv, hkv, 128, dtype, index=303 + hkv)
         w = wl.make_workload(spec, device="cuda")
         g = gpu_balanced(w, step=mode == "step")
         ref = w.value.float().repeat_interleave(4, dim=1)
