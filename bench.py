@@ -43,7 +43,8 @@ METRIC = "decode attention KV-read GB/s (% of HBM peak) and seq-steps/sec at 1 G
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_456_amd", "csrc", f)
-               for f in ("pa_decode.hip", "pa_api.cpp", "pa_internal.h")]
+               for f in ("pa_decode.hip", "pa_decode_balanced.hip", "pa_decode_core.h", "pa_device.h",
+                         "pa_api.cpp", "pa_internal.h")]
 
 
 def log(msg: str) -> None:
