@@ -500,8 +500,11 @@ def bench_prefill(args, dev) -> int:
     visible = int((ql * (L - ql) + ql * (ql + 1) // 2).sum())     # sum over rows of pos + 1
     flops = 4 * D * Hq * visible
 
+    ws = torch.empty(pa.pa_prefill_workspace_size(S, Hq, w.key_cache.shape[1], mq), dtype=torch.uint8,
+                     device=dev)
+
     def call():
-        pa.pa_prefill(out, q, w.key_cache, w.value_cache, bt, cl, qs_d, w.scale, mq)
+        pa.pa_prefill(out, q, w.key_cache, w.value_cache, bt, cl, qs_d, w.scale, mq, ws)
 
     for _ in range(args.warmup):
         call()

@@ -498,18 +498,27 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
  *   Other arguments, alignment and status codes as pa_decode; max_query_len
  *   < 0 or num_query_rows < 0 is PA_EINVAL; num_seqs = 0, max_query_len = 0
  *   or num_query_rows = 0 enqueues nothing.
+ *   workspace        device scratch of at least pa_prefill_workspace_size()
+ *                    bytes, 256-byte aligned (null or smaller:
+ *                    PA_EWORKSPACE); its contents before the call do not
+ *                    matter. The call first orders its work there (the
+ *                    longest contexts' row tiles first); two calls sharing a
+ *                    workspace must not overlap in time. The order never
+ *                    changes a result: every row is computed the same way.
  *   Device-side: a sequence with q_s > L, a context longer than its table
  *   (L > 16 MB) or an empty pool gets NaN rows; a table id outside [0, NB)
  *   within the context gives NaN rows for that sequence (no load leaves the
  *   pool). Nothing is allocated; the call is asynchronous on `stream`.
  */
+size_t pa_prefill_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                 int max_query_len);
 pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query,
                        const void* key_cache, const void* value_cache, pa_dtype_t kv_dtype,
                        const int32_t* block_tables, int max_blocks_per_seq,
                        const int32_t* context_lens, const int32_t* query_start,
                        int64_t num_query_rows, int num_seqs, int num_q_heads, int num_kv_heads,
                        int head_size, int block_size, int64_t num_blocks, float scale,
-                       int max_query_len, void* stream);
+                       int max_query_len, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Block manager -- host-side owner of the pool's blocks and of every

@@ -27,6 +27,6 @@ from ._lib import (  # noqa: F401
     pa_copy_blocks, pa_decode, pa_decode_cascade, pa_decode_cascade_workspace_size,
     pa_decode_partitioned, pa_decode_partitioned_noalloc, pa_decode_partitioned_step,
     pa_decode_partitioned_workspace_size,
-    pa_prefill, pa_reshape_and_cache,
+    pa_prefill, pa_prefill_workspace_size, pa_reshape_and_cache,
     pa_status_str, pa_stream_read, pa_swap_blocks, workspace_partials,
 )

@@ -22,7 +22,8 @@ EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decod
            "pa_decode_balanced", "pa_decode_balanced_workspace_size", "pa_decode_step",
            "pa_decode_partitioned_step",
            "pa_decode_cascade",
-           "pa_decode_cascade_workspace_size", "pa_prefill", "pa_stream_read", "pa_status_str",
+           "pa_decode_cascade_workspace_size", "pa_prefill", "pa_prefill_workspace_size",
+           "pa_stream_read", "pa_status_str",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append_token",
            "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_num_free_blocks", "pa_bm_length",
            "pa_bm_block_table")
@@ -83,7 +84,9 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_cascade_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_cascade_workspace_size.restype = sz
     lib.pa_prefill.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, i64, i32, i32, i32, i32,
-                               i32, i64, f32, i32, vp]
+                               i32, i64, f32, i32, vp, sz, vp]
+    lib.pa_prefill_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.pa_prefill_workspace_size.restype = sz
     lib.pa_prefill.restype = i32
     lib.pa_bm_create.argtypes = [i64, i32]
     lib.pa_bm_create.restype = vp
@@ -259,14 +262,22 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
     return out
 
 
+def pa_prefill_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                              max_query_len: int) -> int:
+    return int(load().pa_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, max_query_len))
+
+
 def pa_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                query_start: torch.Tensor, scale: float, max_query_len: int,
+               workspace: Optional[torch.Tensor] = None,
                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """Multi-token queries over the paged cache. query and out are [T, Hq, D]; the rows of
     sequence s are query_start[s] .. query_start[s + 1] - 1 (int32 [S + 1] on the GPU), the
     last tokens of its context, each attending causally. max_query_len bounds every
-    sequence's row count. out (float32 or bfloat16) is written asynchronously and returned."""
+    sequence's row count. workspace: a uint8 GPU tensor of pa_prefill_workspace_size()
+    bytes (allocated here when None). out (float32 or bfloat16) is written asynchronously
+    and returned."""
     _dev(out, query, key_cache, value_cache, block_tables, context_lens, query_start)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or \
             query_start.dtype != torch.int32:
@@ -280,11 +291,16 @@ def pa_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
         raise TypeError("query and caches must share one dtype")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.shape != (S + 1,):
         raise ValueError("block_tables must be [S, MB] and query_start [S + 1]")
+    if workspace is None:
+        n = pa_prefill_workspace_size(S, Hq, Hkv, max(int(max_query_len), 0))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=query.device)
+    _dev(workspace)
     rc = load().pa_prefill(out.data_ptr(), _dtype_code(out.dtype), query.data_ptr(),
                            key_cache.data_ptr(), value_cache.data_ptr(), _dtype_code(key_cache.dtype),
                            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
                            query_start.data_ptr(), T, S, Hq, Hkv, D, B, NB, float(scale),
-                           int(max_query_len), _stream(query, stream))
+                           int(max_query_len), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), _stream(query, stream))
     _check(rc, "pa_prefill")
     return out
 

@@ -649,12 +649,34 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
     return from_hip(pa::launch_reduce(r, head_size, out_dtype == PA_BF16, num_seqs, s));
 }
 
+// Row tiles per (sequence, KV head) of a prefill call; -1 when out of range.
+static int64_t prefill_row_tiles(int num_q_heads, int num_kv_heads, int max_query_len) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_query_len < 0)
+        return -1;
+    const int64_t rows = static_cast<int64_t>(max_query_len) * (num_q_heads / num_kv_heads);
+    if (rows > INT32_MAX)
+        return -1;
+    constexpr int kTileRows = pa::kPrefillWaves * 16 * pa::kPrefillRowTiles;
+    return (rows + kTileRows - 1) / kTileRows;
+}
+
+size_t pa_prefill_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int max_query_len) {
+    const int64_t tiles = prefill_row_tiles(num_q_heads, num_kv_heads, max_query_len);
+    if (num_seqs < 0 || tiles < 0)
+        return 0;
+    const int64_t pairs = static_cast<int64_t>(num_seqs) * tiles;
+    if (pairs > INT32_MAX || pairs * num_kv_heads > INT32_MAX)
+        return 0;
+    return align256(static_cast<size_t>(pairs) * sizeof(int32_t) + 1);
+}
+
 pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query, const void* key_cache,
                        const void* value_cache, pa_dtype_t kv_dtype, const int32_t* block_tables,
                        int max_blocks_per_seq, const int32_t* context_lens,
                        const int32_t* query_start, int64_t num_query_rows, int num_seqs,
                        int num_q_heads, int num_kv_heads, int head_size, int block_size,
-                       int64_t num_blocks, float scale, int max_query_len, void* stream) {
+                       int64_t num_blocks, float scale, int max_query_len, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     pa_status_t st = check_decode(out, out_dtype, query, key_cache, value_cache, kv_dtype,
                                   block_tables, max_blocks_per_seq, context_lens, num_seqs,
                                   num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
@@ -669,11 +691,14 @@ pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query, const
         return PA_OK;
     if (!query_start || !aligned(query_start, 4))
         return PA_EINVAL;
-    const int64_t rows = static_cast<int64_t>(max_query_len) * (num_q_heads / num_kv_heads);
-    if (rows > INT32_MAX)
+    const int64_t tiles = prefill_row_tiles(num_q_heads, num_kv_heads, max_query_len);
+    const size_t need = pa_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, max_query_len);
+    if (tiles < 0 || need == 0)
         return PA_EUNSUPPORTED;
-    constexpr int kTileRows = pa::kPrefillWaves * 16 * pa::kPrefillRowTiles;
-    const int64_t tiles = (rows + kTileRows - 1) / kTileRows;
+    if (!workspace || workspace_bytes < need)
+        return PA_EWORKSPACE;
+    if (!aligned(workspace, 256))
+        return PA_EINVAL;
     pa::PrefillParams p{};
     p.q = query;
     p.k_cache = key_cache;
@@ -690,6 +715,7 @@ pa_status_t pa_prefill(void* out, pa_dtype_t out_dtype, const void* query, const
     p.group = num_q_heads / num_kv_heads;
     p.max_query_len = max_query_len;
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    p.order = static_cast<int*>(workspace);
     return from_hip(pa::launch_prefill(p, head_size, out_dtype == PA_BF16, num_seqs,
                                        static_cast<int>(tiles), static_cast<hipStream_t>(stream)));
 }

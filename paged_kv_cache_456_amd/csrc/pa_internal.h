@@ -183,7 +183,11 @@ struct PrefillParams {
     int group;
     int max_query_len;             // rows past this many per sequence are not computed
     float scale_log2;              // scale * log2(e)
+    int row_tiles;                 // 128-row tiles per (sequence, KV head)
+    int* order;                    // [S * row_tiles]: (sequence, tile) pairs, most steps first
 };
+
+constexpr int kPrefillOrderBins = 4096;   // step counts the ordering tells apart
 
 struct CopyParams {
     uint8_t* key_cache;

@@ -230,12 +230,12 @@ def test_cascade_workspace_size_formula(lib):
     assert pa.pa_decode_cascade_workspace_size(4, 4, 64, 10, 0, 1) == 0
 
 
-def prefill_call(lib, qs=P, max_q=8, T=32, **kw):
+def prefill_call(lib, qs=P, max_q=8, T=32, ws=P, wsb=1 << 20, **kw):
     a = decode_args(kv_dt=1)
     a.update(kw)
     return lib.pa_prefill(a["out"], a["out_dt"], a["q"], a["kc"], a["vc"], a["kv_dt"], a["bt"],
                           a["MB"], a["cl"], qs, T, a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
-                          a["scale"], max_q, None)
+                          a["scale"], max_q, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,expect", [c for c in DECODE_CASES if "kv_dt" not in c[0]])
@@ -247,9 +247,20 @@ def test_prefill_shares_decode_checks(lib, kw, expect):
     (dict(kv_dt=0), EUNSUP), (dict(max_q=-1), EINVAL), (dict(qs=0), EINVAL), (dict(qs=P + 2), EINVAL),
     (dict(max_q=0, qs=0), OK), (dict(S=0, qs=0), OK), (dict(max_q=1 << 30, Hq=16, Hkv=2), EUNSUP),
     (dict(T=-1), EINVAL), (dict(T=0, qs=0), OK),
+    (dict(ws=0), EWS), (dict(wsb=16), EWS), (dict(ws=P + 16), EINVAL), (dict(ws=0, max_q=0), OK),
 ])
 def test_prefill_checks(lib, kw, expect):
     assert prefill_call(lib, **kw) == expect
+
+
+def test_prefill_workspace_size_formula(lib):
+    a256 = lambda n: (n + 255) // 256 * 256
+    for S, Hq, Hkv, mq in [(64, 32, 8, 512), (1, 4, 4, 1), (3, 16, 1, 100), (7, 8, 2, 0)]:
+        tiles = -(-mq * (Hq // Hkv) // 128)
+        assert pa.pa_prefill_workspace_size(S, Hq, Hkv, mq) == a256(4 * S * tiles + 1)
+    assert pa.pa_prefill_workspace_size(4, 6, 4, 8) == 0
+    assert pa.pa_prefill_workspace_size(-1, 4, 4, 8) == 0
+    assert pa.pa_prefill_workspace_size(4, 16, 2, 1 << 30) == 0
 
 
 @pytest.mark.parametrize("args", [

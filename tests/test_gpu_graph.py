@@ -23,6 +23,8 @@ def test_graph_replays_match_eager(kernel):
     if kernel == "prefill":
         q, qs = wl.prefill_queries(w, [min(int(n), 40) for n in w.context_lens])
         qs = torch.from_numpy(qs).cuda()
+        pws = torch.empty(pa.pa_prefill_workspace_size(S, Hq, w.key_cache.shape[1], 40),
+                          dtype=torch.uint8, device="cuda")
     out = torch.empty((q.shape[0], Hq, D), dtype=torch.float32, device="cuda")
 
     def step():
@@ -32,7 +34,7 @@ def test_graph_replays_match_eager(kernel):
         elif kernel == "single":
             pa.pa_decode(out, q, w.key_cache, w.value_cache, bt, cl, w.scale)
         else:
-            pa.pa_prefill(out, q, w.key_cache, w.value_cache, bt, cl, qs, w.scale, 40)
+            pa.pa_prefill(out, q, w.key_cache, w.value_cache, bt, cl, qs, w.scale, 40, pws)
 
     step()
     torch.cuda.synchronize()
