@@ -41,6 +41,7 @@ using dev::u16x8;
 using dev::u32x4;
 
 constexpr int kStepTokens = 32;                 // two blocks per step
+constexpr float kSlack = 8.0f;                  // base-2 headroom of a row's reference max
 constexpr int kVtStride = kStepTokens + 8;      // bf16 per transposed V row (80 bytes)
 
 template <int D, int NW>
@@ -148,9 +149,10 @@ __device__ __forceinline__ void run_steps(int nsteps, LoadFn load, StageFn stage
     }
 }
 
-// Running state of a wave's RT row tiles: m (base 2) and the partial sum of
-// lane l's tokens for row r16 of each tile, and the output tiles (lane l:
-// row r16, columns 16 n + 4 g + j).
+// Running state of a wave's RT row tiles: the reference maximum m (base 2;
+// every logit seen is at most m + kSlack) and the partial sum of
+// 2^(logit - m) over lane l's tokens for row r16 of each tile, and the output
+// tiles (lane l: row r16, columns 16 n + 4 g + j).
 template <int D, int RT>
 struct RowState {
     float m[RT], lsum[RT];
@@ -197,7 +199,7 @@ __device__ __forceinline__ void split_p(const float (&v)[8], u32x4& hi, u32x4& l
 // logits are dropped by select, never scaled); full(t), the same for every
 // lane of the wave, says that every row of tile t sees all 32 tokens, and
 // skips the selects. The output tiles are rescaled only when some row's
-// maximum moved (a factor of exactly 1 otherwise).
+// reference maximum moves (see kSlack).
 template <int D, int NW, int RT, typename Visible, typename Full>
 __device__ __forceinline__ void attend(const Lds<D, NW>& l, int buf, const u32x4 (&qa)[RT][Shape<D, NW>::NQ],
                                        float scale_log2, Visible visible, Full full, RowState<D, RT>& st) {
@@ -241,9 +243,14 @@ __device__ __forceinline__ void attend(const Lds<D, NW>& l, int buf, const u32x4
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float mn = fmaxf(st.m[t], mx);
+        // The row's reference m moves only when a logit exceeds it by more
+        // than kSlack (P then stays <= 2^kSlack; P, the sum and the output
+        // share the reference, so the result is the same in exact arithmetic)
+        // and the output tiles are rescaled only then.
+        const bool grow = mx > st.m[t] + kSlack;
+        const float mn = grow ? mx : st.m[t];
         // A row that has seen nothing yet (mn = -inf) keeps a zero state.
-        const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m[t] - mn);
+        const float alpha = grow ? __builtin_amdgcn_exp2f(st.m[t] - mn) : 1.0f;
         float pv[8];
         float ps = 0.0f;
 #pragma unroll
@@ -253,7 +260,7 @@ __device__ __forceinline__ void attend(const Lds<D, NW>& l, int buf, const u32x4
         }
         st.lsum[t] = st.lsum[t] * alpha + ps;
         st.m[t] = mn;
-        if (__ballot(alpha != 1.0f) != 0) {
+        if (__ballot(grow) != 0) {
 #pragma unroll
             for (int n = 0; n < NT; ++n)
 #pragma unroll
