@@ -55,14 +55,21 @@
  *  decode calls the softmax weights P stay fp32 through P.V. The dense-tile
  *  calls (the shared-prefix part of pa_decode_cascade, and pa_prefill) run
  *  P.V on bf16 matrix cores with P split into a bf16 high part plus the bf16
- *  rounding of the remainder, which keeps about 16 bits of each weight.
+ *  rounding of the remainder, which keeps about 16 bits of each weight; their
+ *  weights are taken relative to a running reference maximum that moves only
+ *  when a logit exceeds it by 8 (base 2), so a weight is at most 256 before
+ *  the final normalisation (the same result in exact arithmetic).
  *  L = 0 gives a zero row.
  *
  *  Pointers.   All data pointers are DEVICE pointers, 16-byte aligned, owned
  *              by the caller and kept alive until the work on `stream` has
- *              finished. The library allocates nothing, keeps no pointer after
- *              a call returns and holds no state; calls are thread-safe.
- *              `out` and `workspace` must not overlap any input.
+ *              finished. No call allocates memory and none keeps a pointer
+ *              after it returns; the library caches each device's CU count,
+ *              LDS size and kernel occupancies on first use, and
+ *              pa_decode_partitioned_noalloc uses a workspace array the
+ *              library holds on each GPU for the life of the process. Calls
+ *              are thread-safe. `out` and `workspace` must not overlap any
+ *              input.
  *  Streams.    `stream` is a hipStream_t (NULL = the default stream). Every
  *              call only enqueues work and returns; nothing synchronises.
  *  Errors.     Host-side checks run before anything is enqueued and return:
