@@ -200,6 +200,9 @@ __device__ __forceinline__ void split_p(const float (&v)[8], u32x4& hi, u32x4& l
 // lane of the wave, says that every row of tile t sees all 32 tokens, and
 // skips the selects. The output tiles are rescaled only when some row's
 // reference maximum moves (see kSlack).
+// Order: the K Q^T products of every tile and the V^T reads go out first;
+// then tile by tile the softmax (VALU) runs while the matrix core still works
+// on earlier products, and the tile's P V products are issued behind it.
 template <int D, int NW, int RT, typename Visible, typename Full>
 __device__ __forceinline__ void attend(const Lds<D, NW>& l, int buf, const u32x4 (&qa)[RT][Shape<D, NW>::NQ],
                                        float scale_log2, Visible visible, Full full, RowState<D, RT>& st) {
@@ -215,22 +218,35 @@ __device__ __forceinline__ void attend(const Lds<D, NW>& l, int buf, const u32x4
         k0[c] = l.k[buf][r16 * CH + (cc ^ (r16 & (CH - 1)))];
         k1[c] = l.k[buf][(16 + r16) * CH + (cc ^ ((16 + r16) & (CH - 1)))];
     }
-    u32x4 phi[RT], plo[RT];
+    f32x4 a0[RT], a1[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        f32x4 a0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+        a0[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        a1[t] = a0[t];
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
-            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0[c]),
-                                                         __builtin_bit_cast(bf16x8, qa[t][c]), a0, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1[c]),
-                                                         __builtin_bit_cast(bf16x8, qa[t][c]), a1, 0, 0, 0);
+            a0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0[c]),
+                                                            __builtin_bit_cast(bf16x8, qa[t][c]), a0[t], 0, 0, 0);
+            a1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1[c]),
+                                                            __builtin_bit_cast(bf16x8, qa[t][c]), a1[t], 0, 0, 0);
         }
+    }
+    // V^T as the A operand: row 16 n + r16, tokens 4g .. 4g+3 and 16 + 4g .. 16 + 4g + 3.
+    u32x4 va[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const uint16_t* vrow = &l.vt[buf][n * 16 + r16][0];
+        const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow + 4 * g);
+        const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
+        va[n] = u32x4{lo4.x, lo4.y, hi4.x, hi4.y};
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
         float x[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[j] = a0[j] * scale_log2;
-            x[4 + j] = a1[j] * scale_log2;
+            x[j] = a0[t][j] * scale_log2;
+            x[4 + j] = a1[t][j] * scale_log2;
         }
         if (!full(t)) {
 #pragma unroll
@@ -267,21 +283,14 @@ __device__ __forceinline__ void attend(const Lds<D, NW>& l, int buf, const u32x4
                 for (int j = 0; j < 4; ++j)
                     st.o[t][n][j] *= alpha;
         }
-        split_p(pv, phi[t], plo[t]);
-    }
-    // V^T as the A operand: row 16 n + r16, tokens 4g .. 4g+3 and 16 + 4g .. 16 + 4g + 3.
+        u32x4 phi, plo;
+        split_p(pv, phi, plo);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const uint16_t* vrow = &l.vt[buf][n * 16 + r16][0];
-        const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow + 4 * g);
-        const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
-        const u32x4 va = u32x4{lo4.x, lo4.y, hi4.x, hi4.y};
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            st.o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
-                                                                 __builtin_bit_cast(bf16x8, phi[t]), st.o[t][n], 0, 0, 0);
-            st.o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
-                                                                 __builtin_bit_cast(bf16x8, plo[t]), st.o[t][n], 0, 0, 0);
+        for (int n = 0; n < NT; ++n) {
+            st.o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[n]),
+                                                                 __builtin_bit_cast(bf16x8, phi), st.o[t][n], 0, 0, 0);
+            st.o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[n]),
+                                                                 __builtin_bit_cast(bf16x8, plo), st.o[t][n], 0, 0, 0);
         }
     }
 }
