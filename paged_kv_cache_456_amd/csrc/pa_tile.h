@@ -14,7 +14,7 @@
 //     same chunks). The result gives lane l the logits of row r16 for tokens
 //     4g + j (first block) and 16 + 4g + j (second block), j < 4, so each
 //     row's statistics live in the four lanes r16 + 16 g: the row max is an
-//     in-lane max over 8 values and two cross-group exchanges, and m, the
+//     in-lane max over 8 values and two row swaps, and m, the
 //     sum and the rescale factor are one value per lane.
 //   * P V is computed as V^T P^T with the MFMA's 32 k slots mapped to the
 //     step's tokens as slot 8g + i -> token 4g + i (i < 4) and 16 + 4g + i - 4
@@ -169,14 +169,31 @@ struct RowState {
         }
     }
 
-    // Row sum of tile t (every lane of the row's four).
+    // Row sum of tile t (every lane of the row's four), over the same row
+    // swaps as row_group_max.
     __device__ __forceinline__ float row_sum(int t) const {
-        float s = lsum[t];
-        s += __shfl_xor(s, 16, kWave);
-        s += __shfl_xor(s, 32, kWave);
-        return s;
+        const uint32_t u = __float_as_uint(lsum[t]);
+        const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        const float h = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+        const uint32_t w = __float_as_uint(h);
+        const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+        return __uint_as_float(b[0]) + __uint_as_float(b[1]);
     }
 };
+
+// Maximum over the four lanes r16, r16 + 16, r16 + 32, r16 + 48 that hold one
+// row's values, returned to all four: gfx950's row swaps exchange 16-lane
+// rows (and 32-lane halves) between two registers in the VALU, with no LDS
+// round trip. Called with the same value as both operands, each lane gets
+// its own value and its partner's (lane ^ 16, then lane ^ 32).
+__device__ __forceinline__ float row_group_max(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(m);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // P as the B operand, split into bf16 high parts and bf16 remainders, two
 // values per 32-bit word (k slots 2i, 2i + 1 in word i).
@@ -257,8 +274,7 @@ __device__ __forceinline__ void attend(const Lds<D, NW>& l, int buf, const u32x4
         }
         float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        mx = row_group_max(mx);
         // The row's reference m moves only when a logit exceeds it by more
         // than kSlack (P then stays <= 2^kSlack; P, the sum and the output
         // share the reference, so the result is the same in exact arithmetic)
