@@ -405,7 +405,7 @@ pa_status_t pa_decode_partitioned_step(void* out, pa_dtype_t out_dtype, const vo
 /*
  * Workspace bytes pa_decode_cascade needs. With
  *   NPs = max(1, ceil(max(max_context_len - 16 * num_prefix_blocks, 0) / partition_size))
- *   NC  = ceil(num_prefix_blocks / 16),  NP = NPs + NC,  R = S * Hq * NP,
+ *   NC  = ceil(num_prefix_blocks / 32),  NP = NPs + NC,  R = S * Hq * NP,
  * the layout and size formula are those of the partitioned workspace:
  *     2 * round_up(4 R, 256) + round_up(4 R D, 256).
  * Returns 0 when an argument is out of range.
@@ -424,7 +424,7 @@ size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_
  * prefix keys and values are the same for every sequence, so the prefix part
  * of the attention is one dense product per KV head over all S * G query rows
  * (G = Hq / Hkv). This call computes:
- *   1. the prefix, in chunks of 16 blocks, for all query rows at once (K and V
+ *   1. the prefix, in chunks of 32 blocks, for all query rows at once (K and V
  *      read once per KV head, not once per sequence);
  *   2. each sequence's suffix, tokens [16 * num_prefix_blocks, L), through
  *      block-table entries num_prefix_blocks .. MB - 1, in partitions of

@@ -7,15 +7,16 @@
 // and V are the same for all S * G query rows that read that head, so the
 // prefix part of decode attention is a dense product: logits = Q K^T over
 // [S * G rows] x [prefix tokens], and P V. This kernel computes it once per
-// (KV head, 128-row tile, prefix chunk) on MFMA, and writes per-row partials
+// (KV head, 64-row tile, prefix chunk) on MFMA, and writes per-row partials
 // (max m, sum s, normalised output o) of the chunk into the partition slots
 // of the partitioned decode's workspace; the suffix of each sequence is
 // decoded by the paged kernel and the log-sum-exp reduce combines both, so
 // the result is the same attention as a plain decode over the whole context.
 //
-// Per workgroup: 4 waves of two 16-row MFMA tiles each (a wave's share of
-// the step's loads, the V transpose and the barrier serve 32 query rows),
-// one step of 32 prefix tokens (two blocks) at a time, the step of
+// Per workgroup: 4 waves of one 16-row MFMA tile each, over a chunk of 32
+// prefix blocks (a chunk's partials are written once per row, so longer
+// chunks write fewer of them; the combine reads fewer back), one step of 32
+// prefix tokens (two blocks) at a time, the step of
 // pa_tile.h: K and V^T staged in LDS (two buffers, one barrier per step),
 // K Q^T and V^T P^T on v_mfma_f32_16x16x32_bf16 with P kept in registers
 // (split into a bf16 high part and remainder), online softmax per row with

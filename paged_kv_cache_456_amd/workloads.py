@@ -83,7 +83,7 @@ SPECS: Dict[str, WorkloadSpec] = {
     "prefix_shared_bf16": WorkloadSpec(
         3, "prefix_shared_bf16", num_seqs=128, num_q_heads=32, num_kv_heads=8, head_size=128,
         dtype=torch.bfloat16, lengths="prefix:2048,1,512", pool="twice",
-        partition_size=512,
+        partition_size=256,
         description="128 sequences sharing 128 physical prefix blocks (2048 tokens), each with "
                     "a private suffix of uniform [1, 512] tokens whose last block is a "
                     "copy-on-write duplicate of a common parent block"),

@@ -223,7 +223,7 @@ def test_cascade_workspace_size_formula(lib):
                                  (3, 8, 64, 32, 16, 2), (1, 1, 128, 0, 16, 33),
                                  (2, 16, 128, 5000, 256, 64)]:
         sp = max(1, -(-max(L - 16 * npb, 0) // Ps))
-        R = S * Hq * (sp + -(-npb // 16))
+        R = S * Hq * (sp + -(-npb // 32))
         assert pa.pa_decode_cascade_workspace_size(S, Hq, D, L, Ps, npb) == \
             2 * a256(4 * R) + a256(4 * R * D)
     assert pa.pa_decode_cascade_workspace_size(4, 4, 64, 10, 16, 0) == 0

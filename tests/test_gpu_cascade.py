@@ -69,10 +69,10 @@ def test_prefix_shared_workload():
 CASES = [
     # index, S, Hq, Hkv, D, prefix tokens, suffix lo, hi, partition size
     (201, 3, 8, 2, 64, 16, 0, 40, 16),          # one prefix block: a lone block in its step
-    (202, 5, 32, 8, 128, 33 * 16, 0, 100, 32),  # chunks of 16, 16 and a single block
+    (202, 5, 32, 8, 128, 33 * 16, 0, 100, 32),  # chunks of 32 blocks and a single block
     (203, 1, 16, 1, 128, 64 * 16, 1, 1, 16),    # one sequence, group 16
     (204, 70, 4, 4, 64, 40 * 16, 0, 17, 16),    # group 1, two 64-row tiles, ragged
-    (205, 9, 64, 8, 128, 96 * 16, 0, 600, 64),  # group 8, six chunks
+    (205, 9, 64, 8, 128, 96 * 16, 0, 600, 64),  # group 8, three chunks
     (206, 4, 8, 8, 128, 20 * 16, 0, 0, 16),     # every context is exactly the prefix
 ]
 
