@@ -431,6 +431,10 @@ size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_
  *      partition_size tokens (as pa_decode_partitioned);
  *   3. the log-sum-exp combination of the prefix chunks and suffix partitions
  *      (the same formula as pa_decode_partitioned).
+ * Steps 1 and 2 write disjoint workspace slots; when the suffixes run on the
+ * persistent schedule they share one launch (some workgroups take prefix
+ * tiles, the rest decode suffixes), otherwise they are two launches. Either
+ * way the result is the same, bit for bit.
  * The result equals pa_decode on the same inputs, up to fp32 rounding order:
  * the same softmax attention of each query over all L tokens of its context.
  * (The pages name the sharing but give no kernel for it; this split is the

@@ -595,6 +595,9 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
     p.partials_only = 1;
 
     // 1. The shared prefix: one dense pass per KV head for all query rows.
+    // 2. Each sequence's own suffix, through its block table, as partials.
+    // Both write disjoint partial slots; on the persistent schedule they go
+    // out as one launch whose workgroups take either kind of work.
     pa::CascadeParams c{};
     c.q = query;
     c.k_cache = key_cache;
@@ -612,20 +615,28 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
     c.group = p.group;
     c.part_stride = np;
     c.slot_base = sp;
+    c.row_tiles = static_cast<int>((static_cast<int64_t>(num_seqs) * p.group + pa::kCascadeTileRows - 1) /
+                                   pa::kCascadeTileRows);
+    c.num_chunks = ch;
     c.scale_log2 = p.scale_log2;
-    hipError_t e = pa::launch_cascade_prefix(c, head_size, ch, s);
-    if (e != hipSuccess)
-        return PA_EHIP;
-
-    // 2. Each sequence's own suffix, through its block table, as partials.
+    bool shared = false;
+    hipError_t e = hipSuccess;
     if (p.table_blocks > 0) {
         p.persistent = num_seqs <= pa::kMaxPersistentSeqs && num_kv_heads <= pa::kMaxPersistentKvHeads;
         const int waves = choose_waves(p.partition_blocks, elem_bytes(kv_dtype), head_size, p.group,
                                        pa::kPartWaves);
-        e = pa::launch_decode(p, 1, head_size, out_dtype == PA_BF16, num_seqs, sp, waves, s);
-        if (e != hipSuccess)
-            return PA_EHIP;
+        if (p.persistent && waves == pa::kPartWaves)
+            e = pa::launch_cascade_shared(p, c, head_size, out_dtype == PA_BF16, num_seqs, sp, &shared, s);
+        if (e == hipSuccess && !shared) {
+            e = pa::launch_cascade_prefix(c, head_size, s);
+            if (e == hipSuccess)
+                e = pa::launch_decode(p, 1, head_size, out_dtype == PA_BF16, num_seqs, sp, waves, s);
+        }
+    } else {
+        e = pa::launch_cascade_prefix(c, head_size, s);
     }
+    if (e != hipSuccess)
+        return PA_EHIP;
 
     // 3. Log-sum-exp combination of suffix partitions and prefix chunks.
     pa::ReduceParams r{};

@@ -30,6 +30,7 @@
 // positions, so results never depend on where the blocks sit in the pool.
 #include <algorithm>
 
+#include "pa_cascade_tile.h"
 #include "pa_decode_core.h"
 
 namespace pa {
@@ -206,7 +207,7 @@ constexpr int persistent_waves_per_simd() {
     return (GMAX <= 4 && D * KV::kBytes <= 256) ? 3 : 2;
 }
 
-// Persistent schedule: a grid no larger than what the GPU holds at once,
+// Persistent schedule: W workgroups, no more than the GPU holds at once,
 // where workgroup w takes the items w, w + W, w + 2W, ... of the list of
 // (sequence, partition, KV head) items that exist, KV head fastest. The list
 // is built from context_lens in LDS, so no workgroup is spent on the empty
@@ -215,14 +216,10 @@ constexpr int persistent_waves_per_simd() {
 // heads at about the same time (measured faster on MI355X than contiguous,
 // tile-balanced ranges, and than dealing KV head by KV head).
 template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
-__global__ __launch_bounds__(kPartWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(persistent_waves_per_simd<KV, D, GMAX>())))
-void paged_decode_persistent_kernel(DecodeParams p) {
-    extern __shared__ float smem[];
-    const int nw = blockDim.x / kWave;
+__device__ __forceinline__ void persistent_items(const DecodeParams& p, float* smem, int* lens, int wg,
+                                                 int num_wgs) {
     const int lane = threadIdx.x & (kWave - 1);
     const int S = p.num_seqs, Hkv = p.num_kv_heads;
-    int* lens = reinterpret_cast<int*>(smem + decode_lds_floats(KV::kBytes, D, p.group, nw));
     int* first_slot = lens + S;                 // [S + 1], exclusive prefix sum of partitions
     int* list = first_slot + S + 1;             // [kItemListCap][2]: sequence, part << 8 | kvh
     for (int i = threadIdx.x; i < S; i += blockDim.x)
@@ -250,9 +247,9 @@ void paged_decode_persistent_kernel(DecodeParams p) {
     }
     __syncthreads();
     const int64_t items = static_cast<int64_t>(first_slot[S]) * Hkv;
-    for (int64_t k0 = 0; blockIdx.x + k0 * gridDim.x < items; k0 += kItemListCap) {
+    for (int64_t k0 = 0; wg + k0 * num_wgs < items; k0 += kItemListCap) {
         for (int k = threadIdx.x; k < kItemListCap; k += blockDim.x) {
-            const int64_t it = blockIdx.x + (k0 + k) * gridDim.x;
+            const int64_t it = wg + (k0 + k) * num_wgs;
             int seq = -1, pk = 0;
             if (it < items) {
                 const int slot = static_cast<int>(it / Hkv);
@@ -283,6 +280,46 @@ void paged_decode_persistent_kernel(DecodeParams p) {
         }
         __syncthreads();                            // every thread is done with this list
     }
+}
+
+
+template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
+__global__ __launch_bounds__(kPartWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(persistent_waves_per_simd<KV, D, GMAX>())))
+void paged_decode_persistent_kernel(DecodeParams p) {
+    extern __shared__ float smem[];
+    int* lens = reinterpret_cast<int*>(smem + decode_lds_floats(KV::kBytes, D, p.group, blockDim.x / kWave));
+    persistent_items<KV, D, GMAX, OUT, WRITE>(p, smem, lens, blockIdx.x, gridDim.x);
+}
+
+// Shared-prefix batch in one launch: workgroups below tile_wgs take the tiles
+// of the shared-prefix product (tile t = KV head fastest, then 64-row tile,
+// then prefix chunk; workgroup w takes t = w, w + tile_wgs, ...), the others
+// run the persistent schedule over the suffixes. The prefix tiles are bound
+// by their loads' latency and the MFMA step, the suffixes by HBM bandwidth,
+// so the two kinds of work share the CUs instead of following each other.
+// Both write disjoint partial slots of the workspace. The LDS holds either
+// kind's working set at its start, the suffixes' item list behind both.
+template <int D, int GMAX, typename OUT>
+__global__ __launch_bounds__(kPartWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(persistent_waves_per_simd<BF16, D, GMAX>())))
+void cascade_shared_kernel(DecodeParams p, CascadeParams c, int tile_wgs) {
+    extern __shared__ float smem[];
+    static_assert(kPartWaves == kCascadeWaves, "both kinds of work use the same workgroup");
+    if (static_cast<int>(blockIdx.x) < tile_wgs) {
+        auto& lds = *reinterpret_cast<tile::Lds<D, kCascadeWaves>*>(smem);
+        const int tiles = c.num_kv_heads * c.row_tiles * c.num_chunks;
+        for (int t = blockIdx.x; t < tiles; t += tile_wgs) {
+            const int kvh = t % c.num_kv_heads;
+            const int r = t / c.num_kv_heads;
+            tile::prefix_tile<D>(c, lds, kvh, r % c.row_tiles, r / c.row_tiles);
+            __syncthreads();                    // the step's LDS is free for the next tile
+        }
+        return;
+    }
+    int* lens = reinterpret_cast<int*>(smem + cascade_shared_area_floats(D, p.group));
+    persistent_items<BF16, D, GMAX, OUT, false>(p, smem, lens, blockIdx.x - tile_wgs,
+                                                gridDim.x - tile_wgs);
 }
 
 // Log-sum-exp combination of the partitions of every (sequence, KV head)
@@ -472,6 +509,50 @@ hipError_t launch_decode_o(const DecodeParams& p, int out_bf16, int num_seqs, in
                     : launch_decode_g<KV, D, F32>(p, num_seqs, grid_partitions, waves, stream);
 }
 
+template <int D, int GMAX, typename OUT>
+hipError_t launch_cascade_shared_t(const DecodeParams& p, const CascadeParams& c, int num_seqs,
+                                   int grid_partitions, bool* launched, hipStream_t stream) {
+    const auto kernel = cascade_shared_kernel<D, GMAX, OUT>;
+    const size_t lds = sizeof(float) * cascade_shared_area_floats(D, p.group) + persistent_lds_bytes(num_seqs);
+    int dev = 0, per_cu = 0;
+    DeviceInfo info{};
+    *launched = false;
+    hipError_t e = current_device_info(&dev, &info);
+    if (e != hipSuccess || lds > static_cast<size_t>(info.max_lds))
+        return e;
+    e = resident_workgroups_per_cu(dev, reinterpret_cast<const void*>(kernel), kPartWaves * kWave, lds,
+                                   &per_cu);
+    if (e != hipSuccess)
+        return e;
+    // Two tiles per tile workgroup, one tile workgroup per CU at most; the
+    // rest of the resident grid (at least one workgroup, never more than
+    // there can be suffix items) decodes. On the 128-sequence batch with a
+    // 2048-token prefix (256 tiles) this split measured 50.1 us per call, one
+    // tile per workgroup 52.4 us, four 71.2 us (the tiles then finish last).
+    const int tiles = c.num_kv_heads * c.row_tiles * c.num_chunks;
+    const int tile_wgs = std::min((tiles + 1) / 2, info.cus);
+    const int64_t resident = static_cast<int64_t>(info.cus) * std::max(per_cu, 1);
+    const int64_t bound = static_cast<int64_t>(num_seqs) * p.num_kv_heads * grid_partitions;
+    const int64_t decode_wgs = std::max<int64_t>(1, std::min<int64_t>(bound, resident - tile_wgs));
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(tile_wgs + decode_wgs)), dim3(kPartWaves * kWave),
+                       lds, stream, p, c, tile_wgs);
+    e = hipGetLastError();
+    *launched = e == hipSuccess;
+    return e;
+}
+
+template <int D, typename OUT>
+hipError_t launch_cascade_shared_g(const DecodeParams& p, const CascadeParams& c, int num_seqs,
+                                   int grid_partitions, bool* launched, hipStream_t stream) {
+    switch (decode_gmax(p.group)) {
+    case 1: return launch_cascade_shared_t<D, 1, OUT>(p, c, num_seqs, grid_partitions, launched, stream);
+    case 2: return launch_cascade_shared_t<D, 2, OUT>(p, c, num_seqs, grid_partitions, launched, stream);
+    case 4: return launch_cascade_shared_t<D, 4, OUT>(p, c, num_seqs, grid_partitions, launched, stream);
+    case 8: return launch_cascade_shared_t<D, 8, OUT>(p, c, num_seqs, grid_partitions, launched, stream);
+    default: return launch_cascade_shared_t<D, 16, OUT>(p, c, num_seqs, grid_partitions, launched, stream);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_reduce(const ReduceParams& p, int head_size, int out_bf16, int num_seqs,
@@ -501,6 +582,16 @@ hipError_t launch_decode(const DecodeParams& p, int kv_bf16, int head_size, int 
     return head_size == 64
                ? launch_decode_o<F32, 64>(p, out_bf16, num_seqs, grid_partitions, waves, stream)
                : launch_decode_o<F32, 128>(p, out_bf16, num_seqs, grid_partitions, waves, stream);
+}
+
+hipError_t launch_cascade_shared(const DecodeParams& p, const CascadeParams& c, int head_size,
+                                 int out_bf16, int num_seqs, int grid_partitions, bool* launched,
+                                 hipStream_t stream) {
+    if (head_size == 64)
+        return out_bf16 ? launch_cascade_shared_g<64, BF16>(p, c, num_seqs, grid_partitions, launched, stream)
+                        : launch_cascade_shared_g<64, F32>(p, c, num_seqs, grid_partitions, launched, stream);
+    return out_bf16 ? launch_cascade_shared_g<128, BF16>(p, c, num_seqs, grid_partitions, launched, stream)
+                    : launch_cascade_shared_g<128, F32>(p, c, num_seqs, grid_partitions, launched, stream);
 }
 
 }  // namespace pa

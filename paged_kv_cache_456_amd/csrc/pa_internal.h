@@ -15,6 +15,7 @@ constexpr int kReduceThreads = 256;
 constexpr int kCascadeWaves = 4;          // waves per prefix workgroup
 constexpr int kCascadeRowTiles = 1;       // 16-row tiles per wave (64 query rows per workgroup)
 constexpr int kCascadeChunkBlocks = 32;   // prefix blocks per prefix workgroup
+constexpr int kCascadeTileRows = kCascadeWaves * 16 * kCascadeRowTiles;   // query rows per prefix tile
 constexpr int kPrefillWaves = 4;          // waves per multi-token-query workgroup
 constexpr int kPrefillRowTiles = 2;       // 16-row tiles per wave (128 rows per workgroup)
 
@@ -125,6 +126,21 @@ constexpr int kItemListCap = 256;
 constexpr int kMaxPersistentSeqs = 4096;
 constexpr int kMaxPersistentKvHeads = 256;
 // Extra LDS of the persistent schedule: lens [S], first_slot [S + 1], list [cap][2].
+// LDS bytes of the shared-prefix tile step for head size D (K and V^T, two
+// buffers each): 2 * 32 tokens * 2D bytes of K plus 2 * D rows * 40 bf16 of V^T.
+constexpr size_t cascade_tile_lds_bytes(int head_size) {
+    return static_cast<size_t>(288) * head_size;
+}
+
+// The shared launch of a shared-prefix batch (some workgroups take prefix
+// tiles, the others decode suffixes): LDS floats before the suffixes' item
+// list, enough for either kind of work (bf16 KV, kPartWaves waves).
+constexpr size_t cascade_shared_area_floats(int head_size, int group) {
+    return decode_lds_floats(2, head_size, group, kPartWaves) > cascade_tile_lds_bytes(head_size) / 4
+               ? decode_lds_floats(2, head_size, group, kPartWaves)
+               : cascade_tile_lds_bytes(head_size) / 4;
+}
+
 constexpr size_t persistent_lds_bytes(int num_seqs) {
     return sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1 + 2 * kItemListCap);
 }
@@ -163,8 +179,11 @@ struct CascadeParams {
     int group;
     int part_stride;               // row stride of the partials
     int slot_base;                 // slot of prefix chunk 0
+    int row_tiles;                 // 64-row tiles of the S * G query rows of a KV head
+    int num_chunks;                // prefix chunks
     float scale_log2;
 };
+
 
 // Multi-token queries over the paged cache (prompt / chunked prefill).
 struct PrefillParams {
@@ -232,8 +251,13 @@ size_t balanced_lds_bytes_for(int kv_bf16, int head_size, int group, int num_seq
 hipError_t launch_cache(const CacheParams& p, int64_t num_tokens, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, int64_t num_pairs, hipStream_t stream);
 hipError_t launch_swap_blocks(const SwapParams& p, int64_t num_pairs, hipStream_t stream);
-hipError_t launch_cascade_prefix(const CascadeParams& p, int head_size, int num_chunks,
+// One launch for the prefix tiles and the suffixes of a shared-prefix batch
+// (bf16 KV, kPartWaves-wave decode workgroups); *launched is false, and
+// nothing is launched, when its LDS does not fit a workgroup.
+hipError_t launch_cascade_shared(const DecodeParams& p, const CascadeParams& c, int head_size,
+                                 int out_bf16, int num_seqs, int grid_partitions, bool* launched,
                                  hipStream_t stream);
+hipError_t launch_cascade_prefix(const CascadeParams& p, int head_size, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_size, int out_bf16, int num_seqs,
                           int row_tiles, hipStream_t stream);
 int stream_read_waves_per_workgroup();
