@@ -625,8 +625,16 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
         p.persistent = num_seqs <= pa::kMaxPersistentSeqs && num_kv_heads <= pa::kMaxPersistentKvHeads;
         const int waves = choose_waves(p.partition_blocks, elem_bytes(kv_dtype), head_size, p.group,
                                        pa::kPartWaves);
-        if (p.persistent && waves == pa::kPartWaves)
-            e = pa::launch_cascade_shared(p, c, head_size, out_dtype == PA_BF16, num_seqs, sp, &shared, s);
+        if (p.persistent && waves == pa::kPartWaves) {
+            // Beside the suffixes the tiles' latency is hidden, so each takes
+            // a longer chunk (fewer partials to write and combine).
+            pa::CascadeParams cs = c;
+            cs.chunk_blocks = pa::kCascadeSharedChunkBlocks;
+            cs.num_chunks = (num_prefix_blocks + cs.chunk_blocks - 1) / cs.chunk_blocks;
+            e = pa::launch_cascade_shared(p, cs, head_size, out_dtype == PA_BF16, num_seqs, sp, &shared, s);
+            if (shared)
+                c = cs;
+        }
         if (e == hipSuccess && !shared) {
             e = pa::launch_cascade_prefix(c, head_size, s);
             if (e == hipSuccess)
@@ -656,7 +664,7 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
     r.skip_blocks = num_prefix_blocks;
     r.table_blocks = p.table_blocks;
     r.extra_base = sp;
-    r.extra_count = ch;
+    r.extra_count = c.num_chunks;
     return from_hip(pa::launch_reduce(r, head_size, out_dtype == PA_BF16, num_seqs, s));
 }
 

@@ -22,7 +22,9 @@ __device__ __forceinline__ void prefix_tile(const CascadeParams& p, Lds<D, kCasc
                                             int row_tile, int chunk) {
     using S = Shape<D, kCascadeWaves>;
     constexpr int ROW = S::ROW, NQ = S::NQ, NT = S::NT, RT = kCascadeRowTiles;
-    static_assert(kCascadeChunkBlocks <= kWave, "a chunk's block ids fit one per lane");
+    static_assert(kCascadeChunkBlocks <= kWave && kCascadeSharedChunkBlocks <= kWave &&
+                      kCascadeSharedChunkBlocks >= kCascadeChunkBlocks,
+                  "a chunk's block ids fit one per lane; the longer chunks need no more slots");
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);

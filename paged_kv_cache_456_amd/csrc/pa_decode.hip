@@ -524,13 +524,14 @@ hipError_t launch_cascade_shared_t(const DecodeParams& p, const CascadeParams& c
                                    &per_cu);
     if (e != hipSuccess)
         return e;
-    // Two tiles per tile workgroup, one tile workgroup per CU at most; the
+    // One tile per tile workgroup, one tile workgroup per CU at most; the
     // rest of the resident grid (at least one workgroup, never more than
     // there can be suffix items) decodes. On the 128-sequence batch with a
-    // 2048-token prefix (256 tiles) this split measured 50.1 us per call, one
-    // tile per workgroup 52.4 us, four 71.2 us (the tiles then finish last).
+    // 2048-token prefix, 64-block tiles (128 of them, 32 steps each) measured
+    // 46.5 us per call; 32-block tiles 52.4 us at one per workgroup, 50.1 us
+    // at two, 71.2 us at four (the tiles then finish last).
     const int tiles = c.num_kv_heads * c.row_tiles * c.num_chunks;
-    const int tile_wgs = std::min((tiles + 1) / 2, info.cus);
+    const int tile_wgs = std::min(tiles, info.cus);
     const int64_t resident = static_cast<int64_t>(info.cus) * std::max(per_cu, 1);
     const int64_t bound = static_cast<int64_t>(num_seqs) * p.num_kv_heads * grid_partitions;
     const int64_t decode_wgs = std::max<int64_t>(1, std::min<int64_t>(bound, resident - tile_wgs));

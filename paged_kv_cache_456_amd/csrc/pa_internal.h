@@ -14,7 +14,8 @@ constexpr int kPartWaves = 4;    // waves per decode workgroup (partitioned)
 constexpr int kReduceThreads = 256;
 constexpr int kCascadeWaves = 4;          // waves per prefix workgroup
 constexpr int kCascadeRowTiles = 1;       // 16-row tiles per wave (64 query rows per workgroup)
-constexpr int kCascadeChunkBlocks = 32;   // prefix blocks per prefix workgroup
+constexpr int kCascadeChunkBlocks = 32;   // prefix blocks per prefix workgroup (sizes the workspace)
+constexpr int kCascadeSharedChunkBlocks = 64;   // prefix blocks per tile in the shared launch
 constexpr int kCascadeTileRows = kCascadeWaves * 16 * kCascadeRowTiles;   // query rows per prefix tile
 constexpr int kPrefillWaves = 4;          // waves per multi-token-query workgroup
 constexpr int kPrefillRowTiles = 2;       // 16-row tiles per wave (128 rows per workgroup)

@@ -69,17 +69,24 @@ def test_prefix_shared_workload():
 CASES = [
     # index, S, Hq, Hkv, D, prefix tokens, suffix lo, hi, partition size
     (201, 3, 8, 2, 64, 16, 0, 40, 16),          # one prefix block: a lone block in its step
-    (202, 5, 32, 8, 128, 33 * 16, 0, 100, 32),  # chunks of 32 blocks and a single block
+    (202, 5, 32, 8, 128, 33 * 16, 0, 100, 32),  # 32-block chunks and a lone block
     (203, 1, 16, 1, 128, 64 * 16, 1, 1, 16),    # one sequence, group 16
     (204, 70, 4, 4, 64, 40 * 16, 0, 17, 16),    # group 1, two 64-row tiles, ragged
-    (205, 9, 64, 8, 128, 96 * 16, 0, 600, 64),  # group 8, three chunks
+    (205, 9, 64, 8, 128, 96 * 16, 0, 600, 64),  # group 8, three (or 64 + 32-block) chunks
+    (208, 40, 32, 2, 128, 130 * 16, 0, 700, 64),  # group 16, 130 blocks: a 2-block last chunk
     (206, 4, 8, 8, 128, 20 * 16, 0, 0, 16),     # every context is exactly the prefix
 ]
 
 
+# Partitions of 16..64 tokens give suffix workgroups of fewer than four waves
+# (the prefix tiles and the suffixes then run as two launches); 256-token
+# partitions run both in one launch, with 64-block prefix tiles.
+@pytest.mark.parametrize("psize_mode", ["case", "shared"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"w{c[0]}")
-def test_shapes(case):
+def test_shapes(case, psize_mode):
     index, S, Hq, Hkv, D, prefix, lo, hi, psize = case
+    if psize_mode == "shared":
+        psize = 256
     w, npb = prefix_workload(index, S, Hq, Hkv, D, prefix, lo, hi)
     r = oracle_step(w)
     g = gpu_step(w, partition_size=psize, prefix_blocks=npb)
