@@ -124,12 +124,6 @@ def main() -> int:
         return 1
     pa.load()
     dev = torch.device("cuda:0")
-    if args.op == "copy_blocks":
-        return bench_copy_blocks(args, dev)
-    if args.op == "prefill":
-        return bench_prefill(args, dev)
-    if args.op == "swap":
-        return bench_swap(args, dev)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -139,6 +133,12 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: 3 copies of {n} bytes")
         del src, dst
+    if args.op == "copy_blocks":
+        return bench_copy_blocks(args, dev)
+    if args.op == "prefill":
+        return bench_prefill(args, dev)
+    if args.op == "swap":
+        return bench_swap(args, dev)
     stream_read = stream_read_rate(dev, args.stream_read_mib << 20) if args.stream_read_mib > 0 else None
     spec = wl.SPECS[args.workload]
     psize = args.partition_size or spec.partition_size

@@ -67,27 +67,34 @@ __device__ __forceinline__ int prefill_steps(const PrefillParams& p, int s, int 
     return (maxpos / kBlockSize + 2) / 2;
 }
 
-// Orders the (sequence, row tile) pairs by the steps their workgroups run,
-// most first (a counting sort over the step counts in LDS; pairs with equal
-// counts in any order -- every pair's rows are computed the same way
-// wherever it lands). One workgroup.
-__global__ __launch_bounds__(1024) void prefill_order_kernel(PrefillParams p, int num_pairs) {
+// Orders the (sequence, row tile) pairs: sequences by the steps of their
+// longest row tile, most first (a counting sort over those step counts in
+// LDS; sequences with equal counts in any order), and each sequence's row
+// tiles together, its last (longest) tile first. The dispatcher then starts
+// the longest work first, and the tiles of one sequence run at about the same
+// time on their KV head's XCD, where they share the sequence's K and V in L2.
+// A pair's rows are computed the same way wherever it lands, so the order
+// never changes a result. One workgroup.
+__global__ __launch_bounds__(1024) void prefill_order_kernel(PrefillParams p, int num_seqs) {
     constexpr int NB = kPrefillOrderBins;
     constexpr int PER = NB / 1024;             // bins per thread in the scan
     __shared__ int hist[NB];
     __shared__ int start[NB];
     __shared__ int part[1024];
     const int tid = threadIdx.x;
+    const int RT = p.row_tiles;
     for (int i = tid; i < NB; i += 1024)
         hist[i] = 0;
     __syncthreads();
-    auto bin_of = [&](int pr) {
-        const int s = pr / p.row_tiles;
+    auto bin_of = [&](int s) {
+        int most = 0;                          // row tiles' steps do not decrease with the tile
+        for (int t = RT - 1; t >= 0 && most == 0; --t)
+            most = prefill_steps(p, s, t);
         // Bin 0 holds the most steps: the order is ascending in bins.
-        return NB - 1 - min(prefill_steps(p, s, pr - s * p.row_tiles), NB - 1);
+        return NB - 1 - min(most, NB - 1);
     };
-    for (int pr = tid; pr < num_pairs; pr += 1024)
-        atomicAdd(&hist[bin_of(pr)], 1);
+    for (int s = tid; s < num_seqs; s += 1024)
+        atomicAdd(&hist[bin_of(s)], 1);
     __syncthreads();
     // Exclusive prefix sum of hist: each thread sums PER consecutive bins,
     // then a scan of the 1024 partial sums.
@@ -110,8 +117,11 @@ __global__ __launch_bounds__(1024) void prefill_order_kernel(PrefillParams p, in
         run += hist[tid * PER + k];
     }
     __syncthreads();
-    for (int pr = tid; pr < num_pairs; pr += 1024)
-        p.order[atomicAdd(&start[bin_of(pr)], 1)] = pr;
+    for (int s = tid; s < num_seqs; s += 1024) {
+        const int64_t r = atomicAdd(&start[bin_of(s)], 1);    // the sequence's rank
+        for (int j = 0; j < RT; ++j)
+            p.order[r * RT + j] = s * RT + (RT - 1 - j);
+    }
 }
 
 template <int D, typename OUT>
@@ -267,7 +277,7 @@ hipError_t launch_prefill(const PrefillParams& p, int head_size, int out_bf16, i
     PrefillParams q = p;
     q.row_tiles = row_tiles;
     const int num_pairs = num_seqs * row_tiles;
-    hipLaunchKernelGGL(prefill_order_kernel, dim3(1), dim3(1024), 0, stream, q, num_pairs);
+    hipLaunchKernelGGL(prefill_order_kernel, dim3(1), dim3(1024), 0, stream, q, num_seqs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
