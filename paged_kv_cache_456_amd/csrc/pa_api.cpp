@@ -625,7 +625,7 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
         p.persistent = num_seqs <= pa::kMaxPersistentSeqs && num_kv_heads <= pa::kMaxPersistentKvHeads;
         const int waves = choose_waves(p.partition_blocks, elem_bytes(kv_dtype), head_size, p.group,
                                        pa::kPartWaves);
-        if (p.persistent && waves == pa::kPartWaves) {
+        if (p.persistent) {
             // Beside the suffixes the tiles' latency is hidden, so each takes
             // a longer chunk (fewer partials to write and combine).
             pa::CascadeParams cs = c;

@@ -40,26 +40,29 @@ using namespace core;
 
 // Writes the output rows of the head group of KV head `kvh` of sequence `s`
 // when its context has nothing to read: zeros for an empty context, NaN for
-// an unreadable one.
-template <typename OUT>
+// an unreadable one (by the workgroup, or with SOLO by the calling wave).
+template <typename OUT, bool SOLO>
 __device__ __forceinline__ void fill_rows(const DecodeParams& p, int kvh, int s, int D, float v) {
     const int G = p.group;
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int step = SOLO ? kWave : static_cast<int>(blockDim.x);
+    for (int idx = SOLO ? (threadIdx.x & (kWave - 1)) : threadIdx.x; idx < G * D; idx += step) {
         const int h = idx / D, d = idx - (idx / D) * D;
         store_out<OUT>(p.out, ((int64_t)s * p.num_q_heads + kvh * G + h) * D + d, v);
     }
 }
 
 // Blocks [pb0, pb1) of the context of KV head `kvh` of sequence `s` (L > 0
-// tokens, readable), computed by the whole workgroup. With `direct` the range
+// tokens, readable), computed by the whole workgroup, or with SOLO by the
+// calling wave alone (its own LDS slices, no workgroup barrier; the other
+// waves of the workgroup work on other ranges meanwhile). With `direct` the range
 // is the whole context and the output row is written; otherwise the range's
 // (max, sum, normalised output) go to partial slot `slot` of the workspace.
 // With WRITE, the range that holds the context's last token (its new one)
-// streams only the tokens before it from the pool; wave 0 takes the new
-// token's K and V from p.new_key / p.new_value, attends to it and stores it
+// streams only the tokens before it from the pool; wave 0 (or the SOLO wave)
+// takes the new token's K and V from p.new_key / p.new_value, attends to it and stores it
 // in its slot, so the attention never reads the slot being written. All
 // arguments are wave-uniform.
-template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
+template <typename KV, int D, int GMAX, typename OUT, bool WRITE, bool SOLO>
 __device__ __forceinline__ void process_range(const DecodeParams& p, float* smem, int kvh, int s,
                                               int L, int pb0, int pb1, int slot, bool direct) {
     using Gm = Geometry<KV, D>;
@@ -68,7 +71,10 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, float* smem
     constexpr int GP = decode_pstride(GMAX);
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nw = blockDim.x / kWave;
+    const int nwl = blockDim.x / kWave;                         // waves in the LDS layout
+    const int nw = SOLO ? 1 : nwl;                              // waves sharing this range
+    const int w0 = SOLO ? wave : 0;                             // the first of them
+    const bool lead = SOLO || wave == 0;                        // takes the new token
     const int per_round = nw * BPW;
     const int lane = threadIdx.x & (kWave - 1);
     const bool with_new = WRITE && pb1 * kBlockSize >= L;      // the range holds token L - 1
@@ -79,7 +85,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, float* smem
     load_query<KV, D>(p, kvh, s, qa);
     NewToken<KV, D> tok;
     if constexpr (WRITE) {
-        if (with_new && wave == 0) {
+        if (with_new && lead) {
             const int64_t src = ((int64_t)s * p.num_kv_heads + kvh) * ROW;
             tok = load_new_token<KV, D>(static_cast<const char*>(p.new_key) + src,
                                         static_cast<const char*>(p.new_value) + src);
@@ -89,9 +95,9 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, float* smem
     acc.reset();
     if (rounds > 0)
         accumulate_blocks<KV, D, GMAX>(p, smem + wave * (BPW * kBlockSize * GP), qa, kvh, s, L_pool,
-                                       pb1_pool, pb0 + wave * BPW, per_round, rounds, acc);
+                                       pb1_pool, pb0 + (wave - w0) * BPW, per_round, rounds, acc);
     if constexpr (WRITE) {
-        if (with_new && wave == 0) {
+        if (with_new && lead) {
             accumulate_token<KV, D, GMAX>(p, qa, tok, acc);
             store_new_token<KV, D>(p, tok, s, kvh, L, p.skip_blocks);
         }
@@ -109,9 +115,9 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, float* smem
     float (&m)[4] = acc.m;
     float (&o)[GMAX][EPC] = acc.o;
 
-    float* red_m = smem + nw * (BPW * kBlockSize * GP);
-    float* red_s = red_m + nw * GP;
-    float* red_o = red_s + nw * GP;
+    float* red_m = smem + nwl * (BPW * kBlockSize * GP);
+    float* red_s = red_m + nwl * GP;
+    float* red_o = red_s + nwl * GP;
     if (r16 == 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -131,18 +137,23 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, float* smem
                 *reinterpret_cast<f32x4*>(dst + e) = f32x4{o[h][e], o[h][e + 1], o[h][e + 2], o[h][e + 3]};
         }
     }
-    __syncthreads();
+    if constexpr (SOLO)
+        wave_lds_sync();
+    else
+        __syncthreads();
 
-    // Merge the waves in a fixed order.
+    // Merge the waves in a fixed order (a SOLO wave: its own totals, with
+    // weight exp2(0) = 1).
     const bool split = !direct;
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int step = SOLO ? kWave : static_cast<int>(blockDim.x);
+    for (int idx = SOLO ? lane : static_cast<int>(threadIdx.x); idx < G * D; idx += step) {
         const int h = idx / D;
         const int d = idx - h * D;
         float M = -INFINITY;
-        for (int w = 0; w < nw; ++w)
+        for (int w = w0; w < w0 + nw; ++w)
             M = fmaxf(M, red_m[w * GP + h]);
         float S = 0.0f, od = 0.0f;
-        for (int w = 0; w < nw; ++w) {
+        for (int w = w0; w < w0 + nw; ++w) {
             const float f = __builtin_amdgcn_exp2f(red_m[w * GP + h] - M);
             S = fmaf(red_s[w * GP + h], f, S);
             od = fmaf(red_o[(w * GMAX + h) * D + d], f, od);
@@ -171,14 +182,14 @@ __device__ __forceinline__ int schedule_blocks(int L, const DecodeParams& p) {
 }
 
 // Partition `part` of the context of KV head `kvh` of sequence `s`.
-template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
+template <typename KV, int D, int GMAX, typename OUT, bool WRITE, bool SOLO>
 __device__ __forceinline__ void process_partition(const DecodeParams& p, float* smem, int kvh,
                                                   int s, int L, int part) {
     const bool bad = context_unreadable(L, p.table_blocks, p.num_partitions, p.partition_blocks,
                                         p.num_blocks);
     if (bad || L == 0) {
         if (part == 0 && !p.partials_only)
-            fill_rows<OUT>(p, kvh, s, D, bad ? __builtin_nanf("") : 0.0f);
+            fill_rows<OUT, SOLO>(p, kvh, s, D, bad ? __builtin_nanf("") : 0.0f);
         return;
     }
     const int nblk = (L + kBlockSize - 1) / kBlockSize;
@@ -186,7 +197,7 @@ __device__ __forceinline__ void process_partition(const DecodeParams& p, float* 
     const int np = (nblk + PB - 1) / PB;
     if (part >= np)
         return;
-    process_range<KV, D, GMAX, OUT, WRITE>(p, smem, kvh, s, L, part * PB, min((part + 1) * PB, nblk),
+    process_range<KV, D, GMAX, OUT, WRITE, SOLO>(p, smem, kvh, s, L, part * PB, min((part + 1) * PB, nblk),
                                            part, np == 1 && !p.partials_only);
 }
 
@@ -195,7 +206,7 @@ __device__ __forceinline__ void process_partition(const DecodeParams& p, float* 
 template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 __global__ __launch_bounds__(kMaxWaves * kWave) void paged_decode_kernel(DecodeParams p) {
     extern __shared__ float smem[];
-    process_partition<KV, D, GMAX, OUT, WRITE>(p, smem, blockIdx.x, blockIdx.y,
+    process_partition<KV, D, GMAX, OUT, WRITE, false>(p, smem, blockIdx.x, blockIdx.y,
                                                call_len(p.context_lens[blockIdx.y], p.skip_blocks),
                                                blockIdx.z);
 }
@@ -207,14 +218,23 @@ constexpr int persistent_waves_per_simd() {
     return (GMAX <= 4 && D * KV::kBytes <= 256) ? 3 : 2;
 }
 
-// Persistent schedule: W workgroups, no more than the GPU holds at once,
-// where workgroup w takes the items w, w + W, w + 2W, ... of the list of
-// (sequence, partition, KV head) items that exist, KV head fastest. The list
-// is built from context_lens in LDS, so no workgroup is spent on the empty
-// partitions of short sequences. Dealing items round-robin in this order has
-// neighbouring workgroups read the same physical blocks for different KV
-// heads at about the same time (measured faster on MI355X than contiguous,
-// tile-balanced ranges, and than dealing KV head by KV head).
+// Persistent schedule: W workgroups, no more than the GPU holds at once, and
+// their waves are the workers: V = W * NW of them, each taking the items
+// v, v + V, v + 2V, ... of the list of
+// (sequence, partition, KV head) items that exist, KV head fastest. A wave
+// computes its item alone (SOLO), so no wave waits for another between items;
+// the workgroup only shares the list, built from context_lens in LDS, so no
+// worker is spent on the empty partitions of short sequences. With at least
+// as many items as workers, wave j of workgroup w is worker v = w * NW + j
+// (a workgroup's waves take neighbouring items: the same blocks of
+// neighbouring KV heads); with fewer, v = j * W + w, so that the items still
+// spread over every CU instead of filling the first workgroups. Dealing items
+// round-robin in this order has neighbouring waves read the same physical
+// blocks for different KV heads at about the same time. (Measured on MI355X:
+// one wave per item beats a whole workgroup per item -- 201 against 221 us
+// on 8 x 32768-token contexts in 512-token partitions, and about as fast on
+// short ones; a workgroup per item in turn beat contiguous, tile-balanced
+// ranges, and dealing KV head by KV head.)
 template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 __device__ __forceinline__ void persistent_items(const DecodeParams& p, float* smem, int* lens, int wg,
                                                  int num_wgs) {
@@ -247,9 +267,18 @@ __device__ __forceinline__ void persistent_items(const DecodeParams& p, float* s
     }
     __syncthreads();
     const int64_t items = static_cast<int64_t>(first_slot[S]) * Hkv;
-    for (int64_t k0 = 0; wg + k0 * num_wgs < items; k0 += kItemListCap) {
-        for (int k = threadIdx.x; k < kItemListCap; k += blockDim.x) {
-            const int64_t it = wg + (k0 + k) * num_wgs;
+    const int nw = blockDim.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int capw = kItemListCap / nw;         // list entries per wave
+    const int64_t V = static_cast<int64_t>(num_wgs) * nw;
+    const bool blocked = items >= V;
+    auto worker = [&](int w) {
+        return blocked ? static_cast<int64_t>(wg) * nw + w : static_cast<int64_t>(w) * num_wgs + wg;
+    };
+    for (int64_t k0 = 0; worker(0) + k0 * V < items; k0 += capw) {
+        for (int k = threadIdx.x; k < capw * nw; k += blockDim.x) {
+            const int w = k / capw;             // wave w's entries: [w * capw, (w + 1) * capw)
+            const int64_t it = worker(w) + (k0 + (k - w * capw)) * V;
             int seq = -1, pk = 0;
             if (it < items) {
                 const int slot = static_cast<int>(it / Hkv);
@@ -269,19 +298,18 @@ __device__ __forceinline__ void persistent_items(const DecodeParams& p, float* s
             list[2 * k + 1] = pk;
         }
         __syncthreads();
-        for (int k = 0; k < kItemListCap; ++k) {
-            const int seq = __builtin_amdgcn_readfirstlane(list[2 * k]);
+        const int* mine = list + 2 * wave * capw;
+        for (int k = 0; k < capw; ++k) {
+            const int seq = __builtin_amdgcn_readfirstlane(mine[2 * k]);
             if (seq < 0)
                 break;
-            const int pk = __builtin_amdgcn_readfirstlane(list[2 * k + 1]);
-            process_partition<KV, D, GMAX, OUT, WRITE>(p, smem, pk & 0xFF, seq,
-                                                __builtin_amdgcn_readfirstlane(lens[seq]), pk >> 8);
-            __syncthreads();                        // the item's LDS is free again
+            const int pk = __builtin_amdgcn_readfirstlane(mine[2 * k + 1]);
+            process_partition<KV, D, GMAX, OUT, WRITE, true>(p, smem, pk & 0xFF, seq,
+                                                      __builtin_amdgcn_readfirstlane(lens[seq]), pk >> 8);
         }
-        __syncthreads();                            // every thread is done with this list
+        __syncthreads();                            // every wave is done with this list
     }
 }
-
 
 template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 __global__ __launch_bounds__(kPartWaves * kWave)
@@ -457,9 +485,10 @@ hipError_t launch_decode_w(const DecodeParams& p, int num_seqs, int grid_partiti
     if (!p.persistent)
         return launch_decode_grid<KV, D, GMAX, OUT, WRITE>(p, num_seqs, grid_partitions, waves, stream);
     const auto kernel = paged_decode_persistent_kernel<KV, D, GMAX, OUT, WRITE>;
-    // Persistent: as many workgroups as the GPU keeps resident at once (never
-    // more than there can be items).
-    const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, waves) + persistent_lds_bytes(num_seqs);
+    // Persistent: as many kPartWaves-wave workgroups as the GPU keeps resident
+    // at once (never more waves than there can be items); each wave takes its
+    // own items, so the workgroup size does not follow the partition size.
+    const size_t lds = decode_lds_bytes(KV::kBytes, D, p.group, kPartWaves) + persistent_lds_bytes(num_seqs);
     int dev = 0, per_cu = 0;
     DeviceInfo info{};
     hipError_t e = current_device_info(&dev, &info);
@@ -472,14 +501,15 @@ hipError_t launch_decode_w(const DecodeParams& p, int num_seqs, int grid_partiti
         g.persistent = 0;
         return launch_decode_grid<KV, D, GMAX, OUT, WRITE>(g, num_seqs, grid_partitions, waves, stream);
     }
-    e = resident_workgroups_per_cu(dev, reinterpret_cast<const void*>(kernel), waves * kWave, lds,
+    e = resident_workgroups_per_cu(dev, reinterpret_cast<const void*>(kernel), kPartWaves * kWave, lds,
                                    &per_cu);
     if (e != hipSuccess)
         return e;
-    const int64_t bound = static_cast<int64_t>(num_seqs) * p.num_kv_heads * grid_partitions;
+    const int64_t bound = (static_cast<int64_t>(num_seqs) * p.num_kv_heads * grid_partitions + kPartWaves - 1) /
+                          kPartWaves;
     const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(bound, static_cast<int64_t>(info.cus) *
                                                                          std::max(per_cu, 1)));
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(waves * kWave), lds, stream, p);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(kPartWaves * kWave), lds, stream, p);
     return hipGetLastError();
 }
 
@@ -533,7 +563,8 @@ hipError_t launch_cascade_shared_t(const DecodeParams& p, const CascadeParams& c
     const int tiles = c.num_kv_heads * c.row_tiles * c.num_chunks;
     const int tile_wgs = std::min(tiles, info.cus);
     const int64_t resident = static_cast<int64_t>(info.cus) * std::max(per_cu, 1);
-    const int64_t bound = static_cast<int64_t>(num_seqs) * p.num_kv_heads * grid_partitions;
+    const int64_t bound = (static_cast<int64_t>(num_seqs) * p.num_kv_heads * grid_partitions + kPartWaves - 1) /
+                          kPartWaves;
     const int64_t decode_wgs = std::max<int64_t>(1, std::min<int64_t>(bound, resident - tile_wgs));
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(tile_wgs + decode_wgs)), dim3(kPartWaves * kWave),
                        lds, stream, p, c, tile_wgs);
