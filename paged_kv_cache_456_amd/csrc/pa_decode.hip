@@ -351,19 +351,21 @@ void cascade_shared_kernel(DecodeParams p, CascadeParams c, int tile_wgs) {
 }
 
 // Log-sum-exp combination of the partitions of every (sequence, KV head)
-// whose context spans more than one partition: one workgroup per row, one
-// wave per query head at a time. The row's partials are its own partitions
-// followed by any extra slots (shared-prefix chunks), merged 64 at a time:
+// whose context spans more than one partition: one workgroup per (sequence,
+// KV head), one wave per query head of the group. The row's partials are its
+// own partitions followed by any extra slots (shared-prefix chunks), merged
+// 64 at a time:
 //     M = max_i m_i,  w_i = s_i exp(m_i - M),  out = sum_i w_i o_i / sum_i w_i,
 // the running sums rescaled when a later batch raises M. The loads of a batch
 // (maxima, sums and the output rows of up to 16 partials) are all issued
-// before any of them is used; further output rows follow 16 at a time. All
-// reductions run in a fixed order.
+// before any of them is used; further output rows follow 32 at a time. All
+// reductions run in a fixed order (partial by partial), whatever the batching.
 template <int D, typename OUT>
-__global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams p) {
+__global__ __launch_bounds__(kReduceMaxWaves * kWave) void lse_reduce_kernel(ReduceParams p) {
     constexpr int DPL = D / kWave;              // output elements per lane
-    constexpr int PRE = 16;                     // partial outputs loaded together
-    __shared__ int slots[kReduceThreads / kWave][kWave];
+    constexpr int PRE = 16;                     // partial outputs loaded with the statistics
+    constexpr int MORE = 32;                    // partial outputs loaded together after those
+    __shared__ int slots[kReduceMaxWaves][kWave];
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
@@ -439,24 +441,25 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(ReduceParams
                         acc[e] = fmaf(w, ov[j][e], acc[e]);
                 }
             }
-            // The batch's remaining partials, PRE at a time, each group's
+            // The batch's remaining partials, MORE at a time, each group's
             // loads in flight together.
-            for (int j0 = PRE; j0 < n; j0 += PRE) {
+            for (int j0 = PRE; j0 < n; j0 += MORE) {
+                float om[MORE][DPL];
 #pragma unroll
-                for (int j = 0; j < PRE; ++j) {
+                for (int j = 0; j < MORE; ++j) {
                     const int sj = j0 + j < n ? slots[wave][j0 + j] : 0;
                     const float* po = p.part_out + (base + sj) * D + lane;
 #pragma unroll
                     for (int e = 0; e < DPL; ++e)
-                        ov[j][e] = po[e * kWave];
+                        om[j][e] = po[e * kWave];
                 }
 #pragma unroll
-                for (int j = 0; j < PRE; ++j) {
+                for (int j = 0; j < MORE; ++j) {
                     if (j0 + j < n) {
                         const float w = readlane_f(wv, j0 + j);
 #pragma unroll
                         for (int e = 0; e < DPL; ++e)
-                            acc[e] = fmaf(w, ov[j][e], acc[e]);
+                            acc[e] = fmaf(w, om[j][e], acc[e]);
                     }
                 }
             }
@@ -590,16 +593,17 @@ hipError_t launch_cascade_shared_g(const DecodeParams& p, const CascadeParams& c
 hipError_t launch_reduce(const ReduceParams& p, int head_size, int out_bf16, int num_seqs,
                          hipStream_t stream) {
     const dim3 grid(p.num_kv_heads, num_seqs);
+    const dim3 block(std::min(p.group, kReduceMaxWaves) * kWave);
     if (head_size == 64) {
         if (out_bf16)
-            hipLaunchKernelGGL((lse_reduce_kernel<64, BF16>), grid, dim3(kReduceThreads), 0, stream, p);
+            hipLaunchKernelGGL((lse_reduce_kernel<64, BF16>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((lse_reduce_kernel<64, F32>), grid, dim3(kReduceThreads), 0, stream, p);
+            hipLaunchKernelGGL((lse_reduce_kernel<64, F32>), grid, block, 0, stream, p);
     } else {
         if (out_bf16)
-            hipLaunchKernelGGL((lse_reduce_kernel<128, BF16>), grid, dim3(kReduceThreads), 0, stream, p);
+            hipLaunchKernelGGL((lse_reduce_kernel<128, BF16>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((lse_reduce_kernel<128, F32>), grid, dim3(kReduceThreads), 0, stream, p);
+            hipLaunchKernelGGL((lse_reduce_kernel<128, F32>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }

@@ -12,6 +12,7 @@ constexpr int kWave = 64;        // CDNA wavefront width
 constexpr int kMaxWaves = 8;     // waves per decode workgroup (single pass)
 constexpr int kPartWaves = 4;    // waves per decode workgroup (partitioned)
 constexpr int kReduceThreads = 256;
+constexpr int kReduceMaxWaves = 16;      // partition combine: one wave per query head of a group
 constexpr int kCascadeWaves = 4;          // waves per prefix workgroup
 constexpr int kCascadeRowTiles = 1;       // 16-row tiles per wave (64 query rows per workgroup)
 constexpr int kCascadeChunkBlocks = 32;   // prefix blocks per prefix workgroup (sizes the workspace)
