@@ -273,9 +273,13 @@ def main() -> int:
 
     # Duration of the attention call alone: the same K calls again, back to
     # back on the stream they run on, between two HIP events (an event pair
-    # per call would add its own gap to every call).
+    # per call would add its own gap to every call). A short GPU-side wait
+    # ahead of the first event keeps the GPU busy while the host enqueues the
+    # first calls, so the host's launch latency stays outside the timed span.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(100_000)              # ~40 us at the GPU clock
     e0.record()
     for i in range(args.steps):
         attention(inputs[i % len(inputs)])

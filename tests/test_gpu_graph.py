@@ -56,3 +56,54 @@ def test_graph_replays_match_eager(kernel):
         # eager work between replays
         pa.pa_decode(other, w.query, w.key_cache, w.value_cache, bt, cl, w.scale)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kernel", ["cascade", "pstep"])
+def test_graph_replays_match_eager_shared_prefix(kernel):
+    """The shared-prefix call (prefix tiles and suffixes in one launch, then the combine) and
+    the fused decode step, captured and replayed: each replay equals the eager result."""
+    spec = wl.WorkloadSpec(352, "prefix352", num_seqs=12, num_q_heads=32, num_kv_heads=8,
+                           head_size=128, dtype=torch.bfloat16, lengths="prefix:1024,1,300",
+                           pool="twice")
+    w = wl.make_workload(spec, device="cuda")
+    bt, cl, slots = device_inputs(w)
+    S, Hq, D = w.query.shape
+    mcl, P = int(w.max_context_len), 256
+    npb = len(w.shared_blocks)
+    ws = (pa.cascade_workspace(S, Hq, D, mcl, P, npb) if kernel == "cascade"
+          else pa.decode_workspace(S, Hq, D, mcl, P))
+    out = torch.empty((S, Hq, D), dtype=torch.float32, device="cuda")
+    # The step writes each sequence's last token; the cascade reads the cache as it stands.
+    per = spec.new_tokens_per_seq
+    last = torch.arange(S, device="cuda") * per + (per - 1)
+    new_k, new_v = w.key[last].contiguous(), w.value[last].contiguous()
+
+    def step():
+        if kernel == "cascade":
+            pa.pa_decode_cascade(out, w.query, w.key_cache, w.value_cache, bt, cl, w.scale, npb,
+                                 mcl, P, ws)
+        else:
+            pa.pa_decode_partitioned_step(out, w.query, new_k, new_v, w.key_cache, w.value_cache,
+                                          bt, cl, w.scale, mcl, P, ws)
+
+    if kernel == "cascade":
+        pa.pa_reshape_and_cache(w.key, w.value, w.key_cache, w.value_cache, slots)
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = torch.empty((S, Hq, D), dtype=torch.float32, device="cuda")
+    for r in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {r} differs"
+        pa.pa_decode(other, w.query, w.key_cache, w.value_cache, bt, cl, w.scale)
+        torch.cuda.synchronize()
