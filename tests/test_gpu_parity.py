@@ -12,7 +12,7 @@ import torch
 import oracle
 import paged_kv_cache_456_amd as pa
 from paged_kv_cache_456_amd import workloads as wl
-from harness import TOL, check_scatter, device_inputs, gpu_step, max_abs_err, oracle_step
+from harness import TOL, check_scatter, device_inputs, gpu_pstep, gpu_step, max_abs_err, oracle_step
 
 pytestmark = pytest.mark.gpu
 
@@ -208,10 +208,27 @@ def test_sequence_cap(S, G):
         _report(f"S={S} G={G} P={psize}", max_abs_err(g.out, r.out), TOL[torch.bfloat16])
 
 
+@pytest.mark.parametrize("step", [False, True])
+def test_many_items_per_wave(step):
+    """4096 sequences x 8 KV heads in 16-token partitions (~245k items): each wave of the
+    persistent grid takes more items than its share of the LDS item list holds, so the list
+    is rebuilt several times during the call (with the cache write fused, too). Every row
+    against the oracle."""
+    lengths = np.random.default_rng(77).integers(97, 129, 4096).tolist()
+    spec = wl.custom_spec(lengths, 16, 8, 64, torch.bfloat16, index=345)
+    w = wl.make_workload(spec, device="cuda")
+    r = oracle_step(w, partition_size=16)
+    g = gpu_pstep(w, partition_size=16) if step else gpu_step(w, partition_size=16)
+    check_scatter(w, g, r)
+    _report(f"245k items {'step' if step else 'partitioned'}", max_abs_err(g.out, r.out),
+            TOL[torch.bfloat16])
+
+
 def test_reduce_many_partitions():
-    """Rows with more than 16 and more than 64 partitions: the combining kernel loads
-    partials 16 at a time and merges them 64 at a time with rescaling; both must give
-    the single-pass result (fp32 and bf16 KV)."""
+    """Rows with more than 16, more than 48 and more than 64 partitions: the combining
+    kernel loads the first 16 partials with the statistics and the rest 32 at a time, and
+    merges them 64 at a time with rescaling; all must give the single-pass result (fp32 and
+    bf16 KV)."""
     for lengths, hq, hkv, d, dt, psize in (([3000, 1100, 17, 300], 8, 2, 128, torch.bfloat16, 16),
                                            ([2100, 40], 4, 4, 64, torch.float32, 32),
                                            ([1040, 5], 8, 1, 128, torch.bfloat16, 16)):
