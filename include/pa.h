@@ -224,8 +224,10 @@ size_t pa_decode_partitioned_workspace_size(int num_seqs, int num_q_heads, int h
  *
  * Same inputs and result as pa_decode. Each context is cut into partitions of
  * partition_size tokens (a multiple of 16); partition p covers tokens
- * [p * partition_size, min((p + 1) * partition_size, L)). One workgroup per
- * (sequence, KV head, partition) computes the partition's maximum scaled
+ * [p * partition_size, min((p + 1) * partition_size, L)). Each (sequence,
+ * KV head, partition) item -- taken by one wave of a grid of resident
+ * workgroups, or by one workgroup when S > 4096 or the batch's sequence list
+ * does not fit a workgroup's LDS -- computes the partition's maximum scaled
  * logit m_p, sum s_p = sum exp(l_t - m_p) and normalised partial output o_p;
  * a second kernel combines the partitions of each (sequence, KV head), in
  * partition order:
@@ -424,7 +426,7 @@ size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_
  * prefix keys and values are the same for every sequence, so the prefix part
  * of the attention is one dense product per KV head over all S * G query rows
  * (G = Hq / Hkv). This call computes:
- *   1. the prefix, in chunks of 32 blocks, for all query rows at once (K and V
+ *   1. the prefix, in chunks of 32 or 64 blocks, for all query rows at once (K and V
  *      read once per KV head, not once per sequence);
  *   2. each sequence's suffix, tokens [16 * num_prefix_blocks, L), through
  *      block-table entries num_prefix_blocks .. MB - 1, in partitions of
@@ -433,8 +435,9 @@ size_t pa_decode_cascade_workspace_size(int num_seqs, int num_q_heads, int head_
  *      (the same formula as pa_decode_partitioned).
  * Steps 1 and 2 write disjoint workspace slots; when the suffixes run on the
  * persistent schedule they share one launch (some workgroups take prefix
- * tiles, the rest decode suffixes), otherwise they are two launches. Either
- * way the result is the same, bit for bit.
+ * tiles of 64 blocks, the rest decode suffixes), otherwise they are two
+ * launches (prefix chunks of 32 blocks). Both give the same attention, up to
+ * fp32 rounding order.
  * The result equals pa_decode on the same inputs, up to fp32 rounding order:
  * the same softmax attention of each query over all L tokens of its context.
  * (The pages name the sharing but give no kernel for it; this split is the
