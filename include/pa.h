@@ -226,8 +226,8 @@ size_t pa_decode_partitioned_workspace_size(int num_seqs, int num_q_heads, int h
  * partition_size tokens (a multiple of 16); partition p covers tokens
  * [p * partition_size, min((p + 1) * partition_size, L)). Each (sequence,
  * KV head, partition) item -- taken by one wave of a grid of resident
- * workgroups, or by one workgroup when S > 4096 or the batch's sequence list
- * does not fit a workgroup's LDS -- computes the partition's maximum scaled
+ * workgroups, or by one workgroup when S > 4096 or the batch's context
+ * lengths do not fit a workgroup's LDS -- computes the partition's maximum scaled
  * logit m_p, sum s_p = sum exp(l_t - m_p) and normalised partial output o_p;
  * a second kernel combines the partitions of each (sequence, KV head), in
  * partition order:

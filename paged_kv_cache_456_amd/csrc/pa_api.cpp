@@ -344,7 +344,7 @@ static pa_status_t decode_partitioned(void* out, pa_dtype_t out_dtype, const voi
     p.part_stride = np;
     p.table_blocks = max_blocks_per_seq;
     p.num_seqs = num_seqs;
-    p.persistent = num_seqs <= pa::kMaxPersistentSeqs && num_kv_heads <= pa::kMaxPersistentKvHeads;
+    p.persistent = num_seqs <= pa::kMaxPersistentSeqs;
     p.new_key = new_key;
     p.new_value = new_value;
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -622,7 +622,7 @@ pa_status_t pa_decode_cascade(void* out, pa_dtype_t out_dtype, const void* query
     bool shared = false;
     hipError_t e = hipSuccess;
     if (p.table_blocks > 0) {
-        p.persistent = num_seqs <= pa::kMaxPersistentSeqs && num_kv_heads <= pa::kMaxPersistentKvHeads;
+        p.persistent = num_seqs <= pa::kMaxPersistentSeqs;
         const int waves = choose_waves(p.partition_blocks, elem_bytes(kv_dtype), head_size, p.group,
                                        pa::kPartWaves);
         if (p.persistent) {

@@ -12,15 +12,16 @@
 // that spans the whole table. Every query head of the group that shares the
 // KV head is handled by the same wave, so each K/V byte is read from HBM once
 // per step. The partitioned entry point runs a persistent schedule: only as
-// many workgroups as the GPU keeps resident, each taking every grid-th item
-// of the list of items that exist (built from context_lens in LDS); the
-// single pass, and batches too large for that list, use one workgroup per
-// item. An item's blocks are dealt out in rounds: in each round, wave w takes
-// BPW consecutive blocks.
+// many workgroups as the GPU keeps resident, whose waves take every V-th item
+// (V = the grid's waves) of the items that exist, numbered through a prefix
+// sum of the sequences' partition counts built from context_lens in LDS; a
+// wave streams its item's blocks alone, one block per round. The single pass,
+// and batches whose context lengths do not fit a workgroup's LDS, use one
+// workgroup per item instead, its waves taking the item's blocks in turns and
+// merging their (max, sum, output) through LDS in a fixed order.
 //
 // The per-round work of a wave (table resolve, K/V streaming, Q^T K on MFMA,
 // online softmax, P.V) is in pa_decode_core.h.
-// The waves then merge their (max, sum, output) through LDS in a fixed order.
 //
 // Split contexts. A sequence with a single partition writes its output row
 // directly. Otherwise each partition writes its (max, sum, normalised
@@ -218,13 +219,34 @@ constexpr int persistent_waves_per_simd() {
     return (GMAX <= 4 && D * KV::kBytes <= 256) ? 3 : 2;
 }
 
+// The sequence that owns partition slot `slot`: the last s with
+// first_slot[s] <= slot. first_slot is strictly increasing from first_slot[0]
+// = 0 (every sequence counts at least one partition), so the entries at or
+// below the slot form a prefix. A 64-way search: each lane compares one
+// sampled entry, the ballot's population count narrows the range to one
+// sampling interval; one step for S <= 64, two for S <= 4096. Wave-uniform.
+__device__ __forceinline__ int owner_sequence(const int* first_slot, int S, int slot, int lane) {
+    int base = 0, span = S;            // the owner lies in [base, base + span)
+    while (span > kWave) {
+        const int stride = (span + kWave - 1) / kWave;
+        const int off = lane * stride;
+        const bool at_or_below = off < span && first_slot[base + off] <= slot;
+        const int n = __popcll(__ballot(at_or_below));     // >= 1: first_slot[base] <= slot
+        base += (n - 1) * stride;
+        span = min(stride, span - (n - 1) * stride);
+    }
+    const bool at_or_below = lane < span && first_slot[base + lane] <= slot;
+    return base + __popcll(__ballot(at_or_below)) - 1;
+}
+
 // Persistent schedule: W workgroups, no more than the GPU holds at once, and
 // their waves are the workers: V = W * NW of them, each taking the items
-// v, v + V, v + 2V, ... of the list of
-// (sequence, partition, KV head) items that exist, KV head fastest. A wave
-// computes its item alone (SOLO), so no wave waits for another between items;
-// the workgroup only shares the list, built from context_lens in LDS, so no
-// worker is spent on the empty partitions of short sequences. With at least
+// v, v + V, v + 2V, ... of the (sequence, partition, KV head) items that
+// exist, KV head fastest, numbered through the prefix sum of the sequences'
+// partition counts (built once per workgroup in LDS from context_lens), so no
+// worker is spent on the empty partitions of short sequences. A wave finds
+// each of its items' sequence itself (owner_sequence) and computes the item
+// alone (SOLO): after the prefix sum no wave waits for another. With at least
 // as many items as workers, wave j of workgroup w is worker v = w * NW + j
 // (a workgroup's waves take neighbouring items: the same blocks of
 // neighbouring KV heads); with fewer, v = j * W + w, so that the items still
@@ -234,14 +256,17 @@ constexpr int persistent_waves_per_simd() {
 // one wave per item beats a whole workgroup per item -- 201 against 221 us
 // on 8 x 32768-token contexts in 512-token partitions, and about as fast on
 // short ones; a workgroup per item in turn beat contiguous, tile-balanced
-// ranges, and dealing KV head by KV head.)
+// ranges, and dealing KV head by KV head. Finding the items this way instead
+// of through an item list that the workgroup built in LDS, and the prefix sum
+// with DPP row shifts instead of lane shuffles, bring the moment a wave knows
+// its first item from ~2.5 to ~1.4 us after the kernel starts on a 64-sequence
+// batch.)
 template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 __device__ __forceinline__ void persistent_items(const DecodeParams& p, float* smem, int* lens, int wg,
                                                  int num_wgs) {
     const int lane = threadIdx.x & (kWave - 1);
     const int S = p.num_seqs, Hkv = p.num_kv_heads;
     int* first_slot = lens + S;                 // [S + 1], exclusive prefix sum of partitions
-    int* list = first_slot + S + 1;             // [kItemListCap][2]: sequence, part << 8 | kvh
     for (int i = threadIdx.x; i < S; i += blockDim.x)
         lens[i] = call_len(p.context_lens[i], p.skip_blocks);
     __syncthreads();
@@ -251,63 +276,31 @@ __device__ __forceinline__ void persistent_items(const DecodeParams& p, float* s
             const int i = c0 + lane;
             const int nb = i < S ? schedule_blocks(lens[i], p) : 0;
             const int v = (nb + p.partition_blocks - 1) / p.partition_blocks;
-            int incl = v;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const int t = __shfl_up(incl, off, kWave);
-                if (lane >= off)
-                    incl += t;
-            }
+            const int incl = dev::wave_inclusive_sum(v);
             if (i < S)
                 first_slot[i] = carry + incl - v;
-            carry += __shfl(incl, kWave - 1, kWave);
+            carry += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
         if (lane == 0)
             first_slot[S] = carry;
     }
     __syncthreads();
-    const int64_t items = static_cast<int64_t>(first_slot[S]) * Hkv;
+    const int slots = __builtin_amdgcn_readfirstlane(first_slot[S]);
+    const int64_t items = static_cast<int64_t>(slots) * Hkv;
     const int nw = blockDim.x / kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int capw = kItemListCap / nw;         // list entries per wave
     const int64_t V = static_cast<int64_t>(num_wgs) * nw;
-    const bool blocked = items >= V;
-    auto worker = [&](int w) {
-        return blocked ? static_cast<int64_t>(wg) * nw + w : static_cast<int64_t>(w) * num_wgs + wg;
-    };
-    for (int64_t k0 = 0; worker(0) + k0 * V < items; k0 += capw) {
-        for (int k = threadIdx.x; k < capw * nw; k += blockDim.x) {
-            const int w = k / capw;             // wave w's entries: [w * capw, (w + 1) * capw)
-            const int64_t it = worker(w) + (k0 + (k - w * capw)) * V;
-            int seq = -1, pk = 0;
-            if (it < items) {
-                const int slot = static_cast<int>(it / Hkv);
-                const int kvh = static_cast<int>(it - static_cast<int64_t>(slot) * Hkv);
-                int lo = 0, hi = S;                 // last sequence whose first slot <= slot
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (first_slot[mid] <= slot)
-                        lo = mid;
-                    else
-                        hi = mid;
-                }
-                seq = lo;
-                pk = ((slot - first_slot[lo]) << 8) | kvh;
-            }
-            list[2 * k] = seq;
-            list[2 * k + 1] = pk;
-        }
-        __syncthreads();
-        const int* mine = list + 2 * wave * capw;
-        for (int k = 0; k < capw; ++k) {
-            const int seq = __builtin_amdgcn_readfirstlane(mine[2 * k]);
-            if (seq < 0)
-                break;
-            const int pk = __builtin_amdgcn_readfirstlane(mine[2 * k + 1]);
-            process_partition<KV, D, GMAX, OUT, WRITE, true>(p, smem, pk & 0xFF, seq,
-                                                      __builtin_amdgcn_readfirstlane(lens[seq]), pk >> 8);
-        }
-        __syncthreads();                            // every wave is done with this list
+    const int64_t v = items >= V ? static_cast<int64_t>(wg) * nw + wave
+                                 : static_cast<int64_t>(wave) * num_wgs + wg;
+    for (int64_t it = v; it < items; it += V) {
+        const int slot = items <= INT32_MAX
+                             ? static_cast<int>(static_cast<uint32_t>(it) / static_cast<uint32_t>(Hkv))
+                             : static_cast<int>(it / Hkv);
+        const int kvh = static_cast<int>(it - static_cast<int64_t>(slot) * Hkv);
+        const int seq = __builtin_amdgcn_readfirstlane(owner_sequence(first_slot, S, slot, lane));
+        process_partition<KV, D, GMAX, OUT, WRITE, true>(p, smem, kvh, seq,
+                                                  __builtin_amdgcn_readfirstlane(lens[seq]),
+                                                  slot - __builtin_amdgcn_readfirstlane(first_slot[seq]));
     }
 }
 
@@ -327,7 +320,8 @@ void paged_decode_persistent_kernel(DecodeParams p) {
 // by their loads' latency and the MFMA step, the suffixes by HBM bandwidth,
 // so the two kinds of work share the CUs instead of following each other.
 // Both write disjoint partial slots of the workspace. The LDS holds either
-// kind's working set at its start, the suffixes' item list behind both.
+// kind's working set at its start, the suffixes' context lengths and
+// partition prefix sums behind both.
 template <int D, int GMAX, typename OUT>
 __global__ __launch_bounds__(kPartWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(persistent_waves_per_simd<BF16, D, GMAX>())))
@@ -498,7 +492,7 @@ hipError_t launch_decode_w(const DecodeParams& p, int num_seqs, int grid_partiti
     if (e != hipSuccess)
         return e;
     if (lds > static_cast<size_t>(info.max_lds)) {
-        // The sequence list does not fit one workgroup's LDS: one workgroup
+        // The context lengths do not fit one workgroup's LDS: one workgroup
         // per (KV head, sequence, partition) computes the same partials.
         DecodeParams g = p;
         g.persistent = 0;

@@ -37,6 +37,20 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (lane i gets x_0 + ... +
+// x_i): shifts by 1, 2, 4 and 8 lanes within each 16-lane row (a lane with no
+// source adds 0), then lane 15 of rows 0 and 2 added into rows 1 and 3
+// (row_bcast:15) and lane 31 into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+    return x;
+}
+
 // fp32 -> bf16 bits, round to nearest even (for finite values).
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
     uint32_t u = __float_as_uint(x);

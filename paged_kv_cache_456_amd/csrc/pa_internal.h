@@ -122,12 +122,10 @@ constexpr size_t decode_lds_bytes(int elem_bytes, int head_size, int group, int 
     return sizeof(float) * decode_lds_floats(elem_bytes, head_size, group, waves);
 }
 
-// Persistent schedule: items handled per pass over the list, and the largest
-// batch (context lengths and their prefix sums are kept in LDS).
-constexpr int kItemListCap = 256;
+// Persistent schedule: the largest batch (context lengths and their prefix
+// sums are kept in LDS).
 constexpr int kMaxPersistentSeqs = 4096;
-constexpr int kMaxPersistentKvHeads = 256;
-// Extra LDS of the persistent schedule: lens [S], first_slot [S + 1], list [cap][2].
+
 // LDS bytes of the shared-prefix tile step for head size D (K and V^T, two
 // buffers each): 2 * 32 tokens * 2D bytes of K plus 2 * D rows * 40 bf16 of V^T.
 constexpr size_t cascade_tile_lds_bytes(int head_size) {
@@ -135,16 +133,18 @@ constexpr size_t cascade_tile_lds_bytes(int head_size) {
 }
 
 // The shared launch of a shared-prefix batch (some workgroups take prefix
-// tiles, the others decode suffixes): LDS floats before the suffixes' item
-// list, enough for either kind of work (bf16 KV, kPartWaves waves).
+// tiles, the others decode suffixes): LDS floats before the suffixes'
+// context lengths and partition prefix sums, enough for either kind of work
+// (bf16 KV, kPartWaves waves).
 constexpr size_t cascade_shared_area_floats(int head_size, int group) {
     return decode_lds_floats(2, head_size, group, kPartWaves) > cascade_tile_lds_bytes(head_size) / 4
                ? decode_lds_floats(2, head_size, group, kPartWaves)
                : cascade_tile_lds_bytes(head_size) / 4;
 }
 
+// Extra LDS of the persistent schedule: lens [S], first_slot [S + 1].
 constexpr size_t persistent_lds_bytes(int num_seqs) {
-    return sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1 + 2 * kItemListCap);
+    return sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1);
 }
 
 // Work-balanced decode (pa_decode_balanced.hip): the (sequence, KV head,

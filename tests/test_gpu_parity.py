@@ -191,9 +191,10 @@ def test_partitioned_mixed_lengths():
 
 @pytest.mark.parametrize("S,G", [(4096, 16), (4096, 4), (4097, 4)])
 def test_sequence_cap(S, G):
-    """The persistent schedule at its sequence cap, where its sequence list fills most of
-    its LDS (with head group 16 the list and the decode tiles together may exceed one
-    workgroup's LDS, and the launch falls back to one workgroup per item), and one
+    """The persistent schedule at its sequence cap, where the context lengths and their
+    prefix sums fill most of its LDS and each wave finds its items' sequences with the
+    two-level 64-way search (with head group 16 those arrays and the decode tiles together
+    may exceed one workgroup's LDS, and the launch falls back to one workgroup per item), and one
     sequence past the cap (the grid schedule): outputs match the oracle with 16-token
     partitions (up to 3 per context, reduced) and with one partition per context."""
     props = torch.cuda.get_device_properties(0)
@@ -211,9 +212,9 @@ def test_sequence_cap(S, G):
 @pytest.mark.parametrize("step", [False, True])
 def test_many_items_per_wave(step):
     """4096 sequences x 8 KV heads in 16-token partitions (~245k items): each wave of the
-    persistent grid takes more items than its share of the LDS item list holds, so the list
-    is rebuilt several times during the call (with the cache write fused, too). Every row
-    against the oracle."""
+    persistent grid takes dozens of items, finding each one's sequence with the two-level
+    64-way search over the 4096 partition prefix sums (with the cache write fused, too).
+    Every row against the oracle."""
     lengths = np.random.default_rng(77).integers(97, 129, 4096).tolist()
     spec = wl.custom_spec(lengths, 16, 8, 64, torch.bfloat16, index=345)
     w = wl.make_workload(spec, device="cuda")
