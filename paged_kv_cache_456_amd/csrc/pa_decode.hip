@@ -219,88 +219,150 @@ constexpr int persistent_waves_per_simd() {
     return (GMAX <= 4 && D * KV::kBytes <= 256) ? 3 : 2;
 }
 
-// The sequence that owns partition slot `slot`: the last s with
-// first_slot[s] <= slot. first_slot is strictly increasing from first_slot[0]
-// = 0 (every sequence counts at least one partition), so the entries at or
-// below the slot form a prefix. A 64-way search: each lane compares one
-// sampled entry, the ballot's population count narrows the range to one
-// sampling interval; one step for S <= 64, two for S <= 4096. Wave-uniform.
-__device__ __forceinline__ int owner_sequence(const int* first_slot, int S, int slot, int lane) {
-    int base = 0, span = S;            // the owner lies in [base, base + span)
+// #{j < n : a[j] <= x} for a non-decreasing array a (in LDS): a 64-way
+// search in which each lane compares one sampled entry and the ballot's
+// population count narrows the range to one sampling interval (one step for
+// n <= 64, two for n <= 4096). Wave-uniform result. Invariant: a[j] <= x for
+// j < base and a[j] > x for j >= base + span.
+__device__ __forceinline__ int count_at_most(const int* a, int n, int x, int lane) {
+    int base = 0, span = n;
     while (span > kWave) {
         const int stride = (span + kWave - 1) / kWave;
         const int off = lane * stride;
-        const bool at_or_below = off < span && first_slot[base + off] <= slot;
-        const int n = __popcll(__ballot(at_or_below));     // >= 1: first_slot[base] <= slot
-        base += (n - 1) * stride;
-        span = min(stride, span - (n - 1) * stride);
+        const bool le = off < span && a[base + off] <= x;
+        const int k = __popcll(__ballot(le));      // samples 0 .. k-1 are <= x
+        if (k == 0)
+            return base;
+        base += (k - 1) * stride + 1;
+        span = min(stride - 1, span - (k - 1) * stride - 1);
     }
-    const bool at_or_below = lane < span && first_slot[base + lane] <= slot;
-    return base + __popcll(__ballot(at_or_below)) - 1;
+    const bool le = lane < span && a[base + lane] <= x;
+    return base + __popcll(__ballot(le));
 }
 
 // Persistent schedule: W workgroups, no more than the GPU holds at once, and
-// their waves are the workers: V = W * NW of them, each taking the items
-// v, v + V, v + 2V, ... of the (sequence, partition, KV head) items that
-// exist, KV head fastest, numbered through the prefix sum of the sequences'
-// partition counts (built once per workgroup in LDS from context_lens), so no
-// worker is spent on the empty partitions of short sequences. A wave finds
-// each of its items' sequence itself (owner_sequence) and computes the item
-// alone (SOLO): after the prefix sum no wave waits for another. With at least
-// as many items as workers, wave j of workgroup w is worker v = w * NW + j
-// (a workgroup's waves take neighbouring items: the same blocks of
-// neighbouring KV heads); with fewer, v = j * W + w, so that the items still
-// spread over every CU instead of filling the first workgroups. Dealing items
-// round-robin in this order has neighbouring waves read the same physical
-// blocks for different KV heads at about the same time. (Measured on MI355X:
-// one wave per item beats a whole workgroup per item -- 201 against 221 us
-// on 8 x 32768-token contexts in 512-token partitions, and about as fast on
-// short ones; a workgroup per item in turn beat contiguous, tile-balanced
-// ranges, and dealing KV head by KV head. Finding the items this way instead
-// of through an item list that the workgroup built in LDS, and the prefix sum
-// with DPP row shifts instead of lane shuffles, bring the moment a wave knows
-// its first item from ~2.5 to ~1.4 us after the kernel starts on a 64-sequence
-// batch.)
+// their waves are the workers: V = W * NW of them. The (sequence, partition,
+// KV head) items that exist are numbered, KV head fastest, through prefix sums
+// of per-sequence counts that each workgroup builds in LDS from context_lens
+// (so no worker is spent on the empty partitions of short sequences). For up
+// to kMaxSortedSeqs sequences the order is: every full partition (sequence by
+// sequence), then the sequences' last, partly filled partitions in
+// kSizeClasses classes of their block count, largest first; for larger
+// batches, sequence by sequence. Item i goes to worker i mod V in even passes
+// over the workers and to V - 1 - (i mod V) in odd ones, so that a worker
+// that drew a long item early draws a short one late: with several items per
+// wave the busiest wave ends close to the mean. A wave finds each of its
+// items itself (count_at_most over the prefix sums) and computes it alone
+// (SOLO): after the prefix sums no wave waits for another. With at least as
+// many items as workers, wave j of workgroup w is worker v = w * NW + j (a
+// workgroup's waves take neighbouring items: the same blocks of neighbouring
+// KV heads); with fewer, v = j * W + w, so that the items still spread over
+// every CU instead of filling the first workgroups. (Measured on MI355X: one
+// wave per item beats a whole workgroup per item -- 201 against 221 us on 8 x
+// 32768-token contexts in 512-token partitions, and about as fast on short
+// ones; a workgroup per item in turn beat contiguous, tile-balanced ranges,
+// and dealing KV head by KV head. The size-class order with alternating
+// directions against sequence order in one direction: 838 against 854 us on
+// 256 sequences of 1024-8192 tokens in 512-token partitions, 46.1 against
+// 47.8-48.6 us for the suffixes and prefix tiles of the shared-prefix batch.
+// Building the prefix sums with DPP row shifts and finding items by the
+// 64-way search, instead of an item list built in LDS by the whole
+// workgroup, brought the moment a wave knows its first item from ~2.5 to
+// ~1.4 us after the kernel starts on a 64-sequence batch.)
 template <typename KV, int D, int GMAX, typename OUT, bool WRITE>
 __device__ __forceinline__ void persistent_items(const DecodeParams& p, float* smem, int* lens, int wg,
                                                  int num_wgs) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int S = p.num_seqs, Hkv = p.num_kv_heads;
-    int* first_slot = lens + S;                 // [S + 1], exclusive prefix sum of partitions
+    const int S = p.num_seqs, Hkv = p.num_kv_heads, PB = p.partition_blocks;
+    const bool sorted = S <= kMaxSortedSeqs;
+    // sorted: incl[0][s] full partitions of sequences 0..s, incl[1 + c][s]
+    // sequences 0..s whose last partition is partial and of class c;
+    // otherwise incl[0][s] partitions of sequences 0..s. Then the totals.
+    int* incl = lens + S;
+    int* total = incl + (sorted ? 1 + kSizeClasses : 1) * S;
     for (int i = threadIdx.x; i < S; i += blockDim.x)
         lens[i] = call_len(p.context_lens[i], p.skip_blocks);
     __syncthreads();
     if (threadIdx.x < kWave) {
-        int carry = 0;
+        int cf = 0, c01 = 0, c23 = 0;
         for (int c0 = 0; c0 < S; c0 += kWave) {
             const int i = c0 + lane;
             const int nb = i < S ? schedule_blocks(lens[i], p) : 0;
-            const int v = (nb + p.partition_blocks - 1) / p.partition_blocks;
-            const int incl = dev::wave_inclusive_sum(v);
+            int f, p01 = 0, p23 = 0;
+            if (sorted) {
+                f = nb / PB;
+                const int rest = nb - f * PB;
+                const int cls = rest > 0 ? (PB - 1 - rest) * kSizeClasses / PB : -1;
+                p01 = (cls == 0 ? 1 : 0) | (cls == 1 ? 1 << 16 : 0);
+                p23 = (cls == 2 ? 1 : 0) | (cls == 3 ? 1 << 16 : 0);
+            } else {
+                f = (nb + PB - 1) / PB;
+            }
+            const int sf = cf + dev::wave_inclusive_sum(f);
             if (i < S)
-                first_slot[i] = carry + incl - v;
-            carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+                incl[i] = sf;
+            cf = __builtin_amdgcn_readlane(sf, kWave - 1);
+            if (sorted) {
+                // Two class counts per 32-bit word: below 2^16 for S <= kMaxSortedSeqs.
+                const int s01 = c01 + dev::wave_inclusive_sum(p01);
+                const int s23 = c23 + dev::wave_inclusive_sum(p23);
+                if (i < S) {
+                    incl[S + i] = s01 & 0xFFFF;
+                    incl[2 * S + i] = s01 >> 16;
+                    incl[3 * S + i] = s23 & 0xFFFF;
+                    incl[4 * S + i] = s23 >> 16;
+                }
+                c01 = __builtin_amdgcn_readlane(s01, kWave - 1);
+                c23 = __builtin_amdgcn_readlane(s23, kWave - 1);
+            }
         }
-        if (lane == 0)
-            first_slot[S] = carry;
+        if (lane == 0) {
+            total[0] = cf;
+            total[1] = c01 & 0xFFFF;
+            total[2] = c01 >> 16;
+            total[3] = c23 & 0xFFFF;
+            total[4] = c23 >> 16;
+        }
     }
     __syncthreads();
-    const int slots = __builtin_amdgcn_readfirstlane(first_slot[S]);
+    const int full = __builtin_amdgcn_readfirstlane(total[0]);
+    int slots = full;
+    if (sorted) {
+#pragma unroll
+        for (int c = 0; c < kSizeClasses; ++c)
+            slots += __builtin_amdgcn_readfirstlane(total[1 + c]);
+    }
     const int64_t items = static_cast<int64_t>(slots) * Hkv;
     const int nw = blockDim.x / kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t V = static_cast<int64_t>(num_wgs) * nw;
     const int64_t v = items >= V ? static_cast<int64_t>(wg) * nw + wave
                                  : static_cast<int64_t>(wave) * num_wgs + wg;
-    for (int64_t it = v; it < items; it += V) {
+    for (int64_t k = 0;; ++k) {
+        const int64_t it = k * V + ((k & 1) ? V - 1 - v : v);
+        if (it >= items)
+            break;          // only the last pass over the workers is partial
         const int slot = items <= INT32_MAX
                              ? static_cast<int>(static_cast<uint32_t>(it) / static_cast<uint32_t>(Hkv))
                              : static_cast<int>(it / Hkv);
         const int kvh = static_cast<int>(it - static_cast<int64_t>(slot) * Hkv);
-        const int seq = __builtin_amdgcn_readfirstlane(owner_sequence(first_slot, S, slot, lane));
+        int seq, part;
+        if (slot < full) {
+            seq = count_at_most(incl, S, slot, lane);
+            part = slot - (seq > 0 ? incl[seq - 1] : 0);
+        } else {
+            int r = slot - full, c = 0;
+            while (c < kSizeClasses - 1 && r >= total[1 + c]) {
+                r -= total[1 + c];
+                ++c;
+            }
+            seq = count_at_most(incl + (1 + c) * S, S, r, lane);
+            part = incl[seq] - (seq > 0 ? incl[seq - 1] : 0);      // its full partitions
+        }
+        seq = __builtin_amdgcn_readfirstlane(seq);
         process_partition<KV, D, GMAX, OUT, WRITE, true>(p, smem, kvh, seq,
                                                   __builtin_amdgcn_readfirstlane(lens[seq]),
-                                                  slot - __builtin_amdgcn_readfirstlane(first_slot[seq]));
+                                                  __builtin_amdgcn_readfirstlane(part));
     }
 }
 

@@ -123,8 +123,11 @@ constexpr size_t decode_lds_bytes(int elem_bytes, int head_size, int group, int 
 }
 
 // Persistent schedule: the largest batch (context lengths and their prefix
-// sums are kept in LDS).
+// sums are kept in LDS); up to kMaxSortedSeqs sequences the items are ordered
+// by size class (kSizeClasses classes of partly filled last partitions).
 constexpr int kMaxPersistentSeqs = 4096;
+constexpr int kMaxSortedSeqs = 1024;
+constexpr int kSizeClasses = 4;
 
 // LDS bytes of the shared-prefix tile step for head size D (K and V^T, two
 // buffers each): 2 * 32 tokens * 2D bytes of K plus 2 * D rows * 40 bf16 of V^T.
@@ -142,9 +145,12 @@ constexpr size_t cascade_shared_area_floats(int head_size, int group) {
                : cascade_tile_lds_bytes(head_size) / 4;
 }
 
-// Extra LDS of the persistent schedule: lens [S], first_slot [S + 1].
+// Extra LDS of the persistent schedule: lens [S], the inclusive prefix sums
+// ([1 + kSizeClasses][S] when the items are ordered by size class, else [S])
+// and 1 + kSizeClasses totals.
 constexpr size_t persistent_lds_bytes(int num_seqs) {
-    return sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1);
+    return sizeof(int) * ((num_seqs <= kMaxSortedSeqs ? 2 + kSizeClasses : 2) * static_cast<size_t>(num_seqs) +
+                          1 + kSizeClasses);
 }
 
 // Work-balanced decode (pa_decode_balanced.hip): the (sequence, KV head,

@@ -225,6 +225,24 @@ def test_many_items_per_wave(step):
             TOL[torch.bfloat16])
 
 
+@pytest.mark.parametrize("S,step", [(1024, False), (1024, True), (1025, False)])
+def test_items_by_size_class(S, step):
+    """Several items per wave with partly filled last partitions of every size: lengths
+    1..1500 in 128-token partitions (~6 per context, last ones of 1..7 blocks, so all four
+    size classes occur). At the 1024-sequence cap the persistent schedule deals the full
+    partitions first and the partial ones by size class, in alternating directions over the
+    waves; one sequence past the cap it deals them sequence by sequence. Every row against
+    the oracle (and the fused cache write)."""
+    lengths = np.random.default_rng(S + 91).integers(1, 1501, S).tolist()
+    spec = wl.custom_spec(lengths, 8, 4, 64, torch.bfloat16, index=347)
+    w = wl.make_workload(spec, device="cuda")
+    r = oracle_step(w, partition_size=128)
+    g = gpu_pstep(w, partition_size=128) if step else gpu_step(w, partition_size=128)
+    check_scatter(w, g, r)
+    _report(f"size classes S={S} {'step' if step else 'partitioned'}", max_abs_err(g.out, r.out),
+            TOL[torch.bfloat16])
+
+
 def test_reduce_many_partitions():
     """Rows with more than 16, more than 48 and more than 64 partitions: the combining
     kernel loads the first 16 partials with the statistics and the rest 32 at a time, and
