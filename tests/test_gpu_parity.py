@@ -243,6 +243,44 @@ def test_items_by_size_class(S, step):
             TOL[torch.bfloat16])
 
 
+def _random_batch(case):
+    """Seeded batch shape for test_random_batches: sequences, head group, KV heads, head
+    size, KV dtype, partition size and context lengths (some empty, some one block, the rest
+    spread up to 1500 tokens)."""
+    rng = np.random.default_rng(9000 + case)
+    S = int(rng.integers(1, 201))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 4, 8])) if G <= 4 else int(rng.choice([1, 2]))
+    D = int(rng.choice([64, 128]))
+    dtype = torch.float32 if case % 4 == 3 else torch.bfloat16
+    psize = int(rng.choice([16, 32, 64, 128, 256, 512]))
+    kind = rng.random(S)
+    lengths = np.where(kind < 0.05, 0, np.where(kind < 0.15, rng.integers(1, 17, S),
+                                                rng.integers(1, 1501, S)))
+    return S, G, Hkv, D, dtype, psize, [int(v) for v in lengths]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_batches(case):
+    """Seeded random batches (shape, dtype, partition size, length mix with empty and
+    one-block contexts) through the partitioned call and the fused step, every row against the
+    oracle: schedules (items fewer or more than waves, sequence or size-class order) and head
+    groups in combinations the fixed cases do not hit."""
+    S, G, Hkv, D, dtype, psize, lengths = _random_batch(case)
+    print(f"case {case}: S={S} G={G} Hkv={Hkv} D={D} {dtype} P={psize}", flush=True)
+    spec = wl.custom_spec(lengths, G * Hkv, Hkv, D, dtype, index=900 + case)
+    w = wl.make_workload(spec, device="cuda")
+    r = oracle_step(w, partition_size=psize)
+    for step in (False, True):
+        g = gpu_pstep(w, partition_size=psize) if step else gpu_step(w, partition_size=psize)
+        check_scatter(w, g, r)
+        _report(f"random case {case} {'step' if step else 'partitioned'}", max_abs_err(g.out, r.out),
+                TOL[dtype])
+        zero = [s for s, L in enumerate(lengths) if L == 0]
+        if zero:
+            assert torch.equal(g.out[zero], torch.zeros_like(g.out[zero]))
+
+
 def test_reduce_many_partitions():
     """Rows with more than 16, more than 48 and more than 64 partitions: the combining
     kernel loads the first 16 partials with the statistics and the rest 32 at a time, and
