@@ -78,14 +78,15 @@ __device__ __forceinline__ int prefill_steps(const PrefillParams& p, int s, int 
 __global__ __launch_bounds__(1024) void prefill_order_kernel(PrefillParams p, int num_seqs) {
     constexpr int NB = kPrefillOrderBins;
     constexpr int PER = NB / 1024;             // bins per thread in the scan
+    constexpr int NW = 1024 / kWave;
     __shared__ int hist[NB];
     __shared__ int start[NB];
-    __shared__ int part[1024];
+    __shared__ int wave_total[NW];
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
     const int RT = p.row_tiles;
     for (int i = tid; i < NB; i += 1024)
         hist[i] = 0;
-    __syncthreads();
     auto bin_of = [&](int s) {
         int most = 0;                          // row tiles' steps do not decrease with the tile
         for (int t = RT - 1; t >= 0 && most == 0; --t)
@@ -93,24 +94,29 @@ __global__ __launch_bounds__(1024) void prefill_order_kernel(PrefillParams p, in
         // Bin 0 holds the most steps: the order is ascending in bins.
         return NB - 1 - min(most, NB - 1);
     };
-    for (int s = tid; s < num_seqs; s += 1024)
-        atomicAdd(&hist[bin_of(s)], 1);
+    const int my_bin = tid < num_seqs ? bin_of(tid) : 0;     // kept for the scatter below
     __syncthreads();
-    // Exclusive prefix sum of hist: each thread sums PER consecutive bins,
-    // then a scan of the 1024 partial sums.
+    for (int s = tid; s < num_seqs; s += 1024)
+        atomicAdd(&hist[s == tid ? my_bin : bin_of(s)], 1);
+    __syncthreads();
+    // Exclusive prefix sum of hist: each thread sums PER consecutive bins, a
+    // DPP scan within each wave, then one over the waves' totals.
     int local = 0;
 #pragma unroll
     for (int k = 0; k < PER; ++k)
         local += hist[tid * PER + k];
-    part[tid] = local;
+    const int incl = dev::wave_inclusive_sum(local);
+    if (lane == kWave - 1)
+        wave_total[wave] = incl;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int v = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
+    if (wave == 0) {
+        const int t = lane < NW ? wave_total[lane] : 0;
+        const int ti = dev::wave_inclusive_sum(t);
+        if (lane < NW)
+            wave_total[lane] = ti - t;         // exclusive: the bins before this wave's
     }
-    int run = part[tid] - local;
+    __syncthreads();
+    int run = wave_total[wave] + incl - local;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         start[tid * PER + k] = run;
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(1024) void prefill_order_kernel(PrefillParams p, in
     }
     __syncthreads();
     for (int s = tid; s < num_seqs; s += 1024) {
-        const int64_t r = atomicAdd(&start[bin_of(s)], 1);    // the sequence's rank
+        const int64_t r = atomicAdd(&start[s == tid ? my_bin : bin_of(s)], 1);    // the sequence's rank
         for (int j = 0; j < RT; ++j)
             p.order[r * RT + j] = s * RT + (RT - 1 - j);
     }
