@@ -414,14 +414,16 @@ void cascade_shared_kernel(DecodeParams p, CascadeParams c, int tile_wgs) {
 //     M = max_i m_i,  w_i = s_i exp(m_i - M),  out = sum_i w_i o_i / sum_i w_i,
 // the running sums rescaled when a later batch raises M. The loads of a batch
 // (maxima, sums and the output rows of up to 16 partials) are all issued
-// before any of them is used; further output rows follow 32 at a time. All
-// reductions run in a fixed order (partial by partial), whatever the batching.
+// before any of them is used; further output rows follow 32 at a time. A
+// partial's slot is computed from its index (no table); a batch's maximum and
+// weight sum are wave reductions in the VALU (DPP within 16-lane rows, then
+// row swaps), with no LDS round trip. All reductions run in a fixed order
+// (the outputs partial by partial), whatever the batching.
 template <int D, typename OUT>
 __global__ __launch_bounds__(kReduceMaxWaves * kWave) void lse_reduce_kernel(ReduceParams p) {
     constexpr int DPL = D / kWave;              // output elements per lane
     constexpr int PRE = 16;                     // partial outputs loaded with the statistics
     constexpr int MORE = 32;                    // partial outputs loaded together after those
-    __shared__ int slots[kReduceMaxWaves][kWave];
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
@@ -444,6 +446,7 @@ __global__ __launch_bounds__(kReduceMaxWaves * kWave) void lse_reduce_kernel(Red
     if (p.extra_count == 0 && own <= 1)
         return;                                // written directly by its only partition
     const int total = own + p.extra_count;     // partial slots: own partitions, then extras
+    auto slot_of = [&](int i) { return i < own ? i : p.extra_base + (i - own); };
     for (int h = wave; h < G; h += nw) {
         const int64_t row = (int64_t)s * Hq + (int64_t)kvh * G + h;
         const int64_t base = row * p.part_stride;
@@ -455,11 +458,9 @@ __global__ __launch_bounds__(kReduceMaxWaves * kWave) void lse_reduce_kernel(Red
         for (int c0 = 0; c0 < total; c0 += kWave) {
             const int i = c0 + lane;
             const int n = min(kWave, total - c0);
-            slots[wave][lane] = i < own ? i : p.extra_base + (i - own);
-            wave_lds_sync();
             // Lane j < n holds partial j's statistics; the first PRE outputs are
             // requested together with them.
-            const int my = lane < n ? slots[wave][lane] : 0;
+            const int my = lane < n ? slot_of(i) : 0;
             const float mv = lane < n ? p.part_max[base + my] : -INFINITY;
             const float sv = lane < n ? p.part_sum[base + my] : 0.0f;
             float ov[PRE][DPL];
@@ -467,23 +468,17 @@ __global__ __launch_bounds__(kReduceMaxWaves * kWave) void lse_reduce_kernel(Red
             for (int j = 0; j < PRE; ++j) {
                 // Past the batch's partials the load re-reads slot 0 of the row
                 // (always inside the workspace); the value is not used.
-                const int sj = j < n ? slots[wave][j] : 0;
+                const int sj = j < n ? slot_of(c0 + j) : 0;
                 const float* po = p.part_out + (base + sj) * D + lane;
 #pragma unroll
                 for (int e = 0; e < DPL; ++e)
                     ov[j][e] = po[e * kWave];
             }
-            float cm = mv;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1)
-                cm = fmaxf(cm, __shfl_xor(cm, o, kWave));
+            const float cm = dev::wave_max(mv);
             const float Mn = fmaxf(M, cm);
             const float scale = M == Mn ? 1.0f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
             const float wv = lane < n ? sv * __builtin_amdgcn_exp2f((mv - Mn) * kLog2e) : 0.0f;
-            float ws = wv;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1)
-                ws += __shfl_xor(ws, o, kWave);
+            const float ws = dev::wave_sum(wv);
             T = T * scale + ws;
 #pragma unroll
             for (int e = 0; e < DPL; ++e)
@@ -503,7 +498,7 @@ __global__ __launch_bounds__(kReduceMaxWaves * kWave) void lse_reduce_kernel(Red
                 float om[MORE][DPL];
 #pragma unroll
                 for (int j = 0; j < MORE; ++j) {
-                    const int sj = j0 + j < n ? slots[wave][j0 + j] : 0;
+                    const int sj = j0 + j < n ? slot_of(c0 + j0 + j) : 0;
                     const float* po = p.part_out + (base + sj) * D + lane;
 #pragma unroll
                     for (int e = 0; e < DPL; ++e)
@@ -520,7 +515,6 @@ __global__ __launch_bounds__(kReduceMaxWaves * kWave) void lse_reduce_kernel(Red
                 }
             }
             M = Mn;
-            wave_lds_sync();
         }
 #pragma unroll
         for (int e = 0; e < DPL; ++e)

@@ -37,6 +37,31 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// Max / sum over the 64 lanes of a wave, returned to every lane: the 16-lane
+// row reductions above, then gfx950's row swaps (v_permlane16_swap pairs lane
+// l with l ^ 16, v_permlane32_swap with l ^ 32; called with the same value as
+// both operands, each lane gets its own value and its partner's), all in the
+// VALU. A fixed order: the same inputs always give the same bits.
+__device__ __forceinline__ float wave_max(float x) {
+    x = row_max16(x);
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row_sum16(x);
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t w = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (lane i gets x_0 + ... +
 // x_i): shifts by 1, 2, 4 and 8 lanes within each 16-lane row (a lane with no
 // source adds 0), then lane 15 of rows 0 and 2 added into rows 1 and 3
